@@ -1,0 +1,81 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin fails.
+
+Each mutation replaces one oracle function with a wrong variant for the length
+of one check; the pin it is paired with must notice.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import vsa_oracle as vo
+
+from test_oracle_pins import _dense_masked, _random_topk, _tiled_case
+
+
+def _fwd_no_vbs(q_t, k_t, v_t, topk_idx, vbs, b, h, c, sm_scale=None):
+    full = np.full_like(np.asarray(vbs), 64)          # padding not masked
+    return _orig_fwd_unit(q_t, k_t, v_t, topk_idx, full, b, h, c, sm_scale)
+
+
+def _fwd_wrong_scale(q_t, k_t, v_t, topk_idx, vbs, b, h, c, sm_scale=None):
+    return _orig_fwd_unit(q_t, k_t, v_t, topk_idx, vbs, b, h, c, 1.0 / q_t.shape[-1])
+
+
+def _fwd_transposed_kv(q_t, k_t, v_t, topk_idx, vbs, b, h, c, sm_scale=None):
+    return _orig_fwd_unit(q_t, v_t, k_t, topk_idx, vbs, b, h, c, sm_scale)
+
+
+_orig_fwd_unit = vo.fwd_unit
+
+
+def _pin_dense(monkeypatch, mutant):
+    monkeypatch.setattr(vo, "fwd_unit", mutant)
+    q, k, v, vbs = _tiled_case(5, 6, 7, NH=2, D=16)
+    idx = _random_topk(1, 2, 8, 3)
+    got = vo.fwd(q, k, v, idx, vbs)
+    ref = _dense_masked(q, k, v, idx, vbs, 1 / math.sqrt(16))
+    return np.max(np.abs(got - ref))
+
+
+@pytest.mark.parametrize("mutant", [_fwd_no_vbs, _fwd_wrong_scale, _fwd_transposed_kv])
+def test_dense_pin_catches_fwd_mutations(monkeypatch, mutant):
+    assert _pin_dense(monkeypatch, mutant) > 1e-6
+
+
+def test_dense_pin_passes_unmutated(monkeypatch):
+    assert _pin_dense(monkeypatch, _orig_fwd_unit) < 1e-12
+
+
+def test_pool_pin_catches_denominator_64(monkeypatch):
+    orig = vo.mean_pool
+
+    def pool64(x_t, vbs):
+        return orig(x_t, vbs) * (np.asarray(vbs, np.float64)[None, None, :, None] / 64.0)
+
+    monkeypatch.setattr(vo, "mean_pool", pool64)
+    vbs = oracle.cube_sizes(5, 6, 7)
+    const = np.full((1, 8 * 64, 1, 3), 0.7)
+    assert np.max(np.abs(vo.mean_pool(const, vbs) - 0.7)) > 0.1
+
+
+def test_topk_pin_catches_unstable_tie_order(monkeypatch):
+    def topk_desc_ties_high(S, k):
+        order = np.argsort(-S[..., ::-1], axis=-1, kind="stable")
+        return (S.shape[-1] - 1 - order[..., :k]).astype(np.int32)
+
+    from test_oracle_pins import _rank_count_topk
+    S = np.array([[[[1.0, 2.0, 2.0, 0.0, 2.0]]]])
+    assert not np.array_equal(topk_desc_ties_high(S, 2)[0, 0, 0], _rank_count_topk(S[0, 0, 0], 2))
+    np.testing.assert_array_equal(vo.topk_select(S, 2)[0, 0, 0], _rank_count_topk(S[0, 0, 0], 2))
+
+
+def test_tile_pin_catches_column_major_cube_order():
+    T, H, W = 5, 6, 7
+    good = oracle.slot_tokens(T, H, W)
+    # cube ids enumerated with w slowest instead of t slowest
+    Nt, Nh, Nw = oracle.cube_grid(T, H, W)
+    perm = [((cw * Nh + ch) * Nt + ct) for ct in range(Nt) for ch in range(Nh) for cw in range(Nw)]
+    bad = good[np.argsort(perm)]
+    assert not np.array_equal(bad, good)

@@ -1,0 +1,372 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the oracle.
+
+Each test ties one oracle function to something other than itself: numbers the
+pages print, closed forms derived by hand, an independent formulation (brute
+force, a library routine), or an invariant of the mathematics. Run on the CPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+RNG = np.random.default_rng(1234)
+
+
+def _randn(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+# ------------------------------------------------------------------ tiling
+
+def test_printed_counts_wan_grid():
+    """Dataset card "Shapes": S_padded = 39936 = 624 x 64, real = 32760 = 21x30x52,
+    Nq = Nkv = 624 = 6 x 8 x 13."""
+    assert oracle.cube_grid(21, 30, 52) == (6, 8, 13)
+    vbs = oracle.cube_sizes(21, 30, 52)
+    assert vbs.shape == (624,)
+    assert vbs.size * 64 == 39936
+    assert int(vbs.sum()) == 32760
+
+
+def test_printed_counts_720p_grid():
+    """FastVideo STA guide, "The 115K Token Sequence Wall": latent (30, 48, 80)
+    gives N = 115,200 tokens."""
+    vbs = oracle.cube_sizes(30, 48, 80)
+    assert vbs.size == 8 * 12 * 20
+    assert int(vbs.sum()) == 115200
+
+
+@pytest.mark.parametrize("grid,hist", [
+    # 21 = 5*4 + 1, 30 = 7*4 + 2, 52 = 13*4: cube sizes are et*eh*4 with
+    # et in {4 (5 cubes), 1 (1 cube)}, eh in {4 (7 cubes), 2 (1 cube)}, 13 cw.
+    ((21, 30, 52), {64: 5 * 7 * 13, 32: 5 * 1 * 13, 16: 1 * 7 * 13, 8: 1 * 1 * 13}),
+    # 30 = 7*4 + 2, 48 = 12*4, 80 = 20*4
+    ((30, 48, 80), {64: 7 * 12 * 20, 32: 1 * 12 * 20}),
+])
+def test_vbs_histogram_closed_form(grid, hist):
+    vbs = oracle.cube_sizes(*grid)
+    vals, counts = np.unique(vbs, return_counts=True)
+    assert dict(zip(vals.tolist(), counts.tolist())) == hist
+
+
+def test_vbs_tiny_row_major_order():
+    """5x6x7: extents t (4, 1), h (4, 2), w (4, 3); cube id (ct*Nh + ch)*Nw + cw."""
+    expect = [4 * 4 * 4, 4 * 4 * 3, 4 * 2 * 4, 4 * 2 * 3,
+              1 * 4 * 4, 1 * 4 * 3, 1 * 2 * 4, 1 * 2 * 3]
+    assert oracle.cube_sizes(5, 6, 7).tolist() == expect
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (4, 4, 4), (1, 1, 1), (9, 3, 5), (8, 13, 2)])
+def test_tile_permutation_independent_derivation(grid):
+    """Token -> slot by sorting tokens on (cube id, t, h, w): an independent
+    formulation of the cube-major order with real tokens first, row-major inside
+    the clipped cube."""
+    T, H, W = grid
+    Nt, Nh, Nw = -(-T // 4), -(-H // 4), -(-W // 4)
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    t, y, x = t.ravel(), y.ravel(), x.ravel()
+    nat = (t * H + y) * W + x
+    cube = ((t // 4) * Nh + y // 4) * Nw + x // 4
+    order = np.lexsort((x, y, t, cube))          # primary key: cube
+    expect = np.full((Nt * Nh * Nw, 64), -1)
+    for c in range(Nt * Nh * Nw):
+        members = nat[order][cube[order] == c]
+        expect[c, :members.size] = members
+    np.testing.assert_array_equal(oracle.slot_tokens(T, H, W), expect)
+
+
+def test_tile_untile_roundtrip_bitwise_and_zero_pads():
+    T, H, W = 5, 6, 7
+    x = RNG.integers(0, 2 ** 16, size=(2, T * H * W, 3, 8), dtype=np.uint16)
+    xt, vbs = oracle.tile(x, T, H, W)
+    assert xt.shape == (2, 8 * 64, 3, 8) and xt.dtype == np.uint16
+    for c in range(8):
+        assert np.all(xt[:, 64 * c + vbs[c]:64 * (c + 1)] == 0)
+    np.testing.assert_array_equal(oracle.untile(xt, T, H, W), x)
+
+
+# ---------------------------------------------------------------- bf16 values
+
+def test_decode_bf16_known_values():
+    bits = np.array([0x3F80, 0xBF80, 0x4000, 0x0000, 0x8000, 0x7F7F, 0x0001], np.uint16)
+    expect = [1.0, -1.0, 2.0, 0.0, -0.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133]
+    np.testing.assert_array_equal(oracle.decode_bf16(bits), expect)
+
+
+def test_round_to_bf16_ties_and_library():
+    # ties to even at 1 + 2^-8 (halfway between 1 and 1 + 2^-7)
+    cases = {1 + 2 ** -8: 1.0, 1 + 3 * 2 ** -8: 1 + 2 ** -6, -(1 + 2 ** -8): -1.0,
+             1 + 2 ** -8 + 2 ** -30: 1 + 2 ** -7,
+             2.0 ** -140: 0.0,                 # below half the smallest subnormal
+             3 * 2.0 ** -134: 2.0 ** -132,     # subnormal tie -> even multiple
+             (2 - 2 ** -9) * 2.0 ** 127: math.inf}
+    for x, r in cases.items():
+        got = float(oracle.round_to_bf16(np.array([x]))[0])
+        assert got == r, (x, got, r)
+    # float32-representable inputs: torch's float32 -> bfloat16 conversion
+    x = (RNG.standard_normal(20000) * np.exp(RNG.uniform(-30, 30, 20000))).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_to_bf16(x.astype(np.float64)), lib)
+
+
+# ------------------------------------------------------------- fine stage
+
+def _dense_masked(q_t, k_t, v_t, topk_idx, vbs, scale):
+    """Brute force: full S_padded x S_padded score matrix with the block mask
+    M[i, j] = cube(j) in sel(cube(i)) and slot(j) < vbs[cube(j)]."""
+    B, S, NH, D = q_t.shape
+    cube_of = np.arange(S) // 64
+    slot_of = np.arange(S) % 64
+    out = np.zeros_like(q_t)
+    for b in range(B):
+        for h in range(NH):
+            sel = np.zeros((S // 64, S // 64), bool)
+            for c in range(S // 64):
+                sel[c, topk_idx[b, h, c]] = True
+            M = sel[cube_of][:, cube_of] & (slot_of < vbs[cube_of])[None, :]
+            s = q_t[b, :, h] @ k_t[b, :, h].T * scale
+            s = np.where(M, s, -np.inf)
+            s -= s.max(axis=1, keepdims=True)
+            p = np.where(M, np.exp(s), 0.0)
+            out[b, :, h] = p @ v_t[b, :, h] / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def _tiled_case(T, H, W, NH, D, B=1, rng=RNG):
+    vbs = oracle.cube_sizes(T, H, W)
+    Nc = vbs.size
+    q = _randn(B, Nc * 64, NH, D, rng=rng)
+    k = _randn(B, Nc * 64, NH, D, rng=rng)
+    v = _randn(B, Nc * 64, NH, D, rng=rng)
+    return q, k, v, vbs
+
+
+def _random_topk(B, NH, Nc, k, rng=RNG):
+    return np.stack([np.stack([np.stack([rng.permutation(Nc)[:k] for _ in range(Nc)])
+                               for _ in range(NH)]) for _ in range(B)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("grid,k,D", [((5, 6, 7), 3, 16), ((9, 5, 6), 4, 8), ((4, 8, 4), 1, 8)])
+def test_fwd_equals_dense_masked_softmax(grid, k, D):
+    q, kk, v, vbs = _tiled_case(*grid, NH=2, D=D, B=2)
+    idx = _random_topk(2, 2, vbs.size, k)
+    got = oracle.fwd(q, kk, v, idx, vbs)
+    ref = _dense_masked(q, kk, v, idx, vbs, 1 / math.sqrt(D))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_fwd_topk_all_full_cubes_equals_sdpa():
+    """8x8x8 grid: all cubes full; topk = all cubes is dense attention over the
+    tiled sequence (torch CPU float64 scaled_dot_product_attention)."""
+    T = H = W = 8
+    q, k, v, vbs = _tiled_case(T, H, W, NH=2, D=32)
+    assert np.all(vbs == 64)
+    idx = np.tile(np.arange(8, dtype=np.int32), (1, 2, 8, 1))
+    got = oracle.fwd(q, k, v, idx, vbs)
+    tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).permute(0, 2, 1, 3)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_fwd_topk_all_partial_cubes_equals_sdpa_on_real_tokens():
+    """With partial cubes, topk = all equals dense attention over the real
+    tokens in natural order (the padding deleted), for every real row."""
+    T, H, W = 5, 6, 7
+    NH, D = 3, 16
+    qn, kn, vn = (_randn(1, T * H * W, NH, D) for _ in range(3))
+    qt, vbs = oracle.tile(qn, T, H, W)
+    kt, _ = oracle.tile(kn, T, H, W)
+    vt, _ = oracle.tile(vn, T, H, W)
+    idx = np.tile(np.arange(8, dtype=np.int32)[::-1], (1, NH, 8, 1))
+    got = oracle.untile(oracle.fwd(qt, kt, vt, idx, vbs), T, H, W)
+    tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3) for a in (qn, kn, vn))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).permute(0, 2, 1, 3)
+    np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("poison", [np.nan, 1e30, -np.inf])
+def test_fwd_ignores_padding_values(poison):
+    """Masking by vbs is the same as deleting the padding: poisoned padding
+    slots of k and v leave every output row unchanged (bit for bit)."""
+    q, k, v, vbs = _tiled_case(5, 6, 7, NH=2, D=16)
+    idx = _random_topk(1, 2, 8, 5)
+    ref = oracle.fwd(q, k, v, idx, vbs)
+    k2, v2 = k.copy(), v.copy()
+    for c in range(8):
+        k2[:, 64 * c + vbs[c]:64 * (c + 1)] = poison
+        v2[:, 64 * c + vbs[c]:64 * (c + 1)] = poison
+    got = oracle.fwd(q, k2, v2, idx, vbs)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_fwd_order_invariance():
+    q, k, v, vbs = _tiled_case(9, 5, 6, NH=2, D=16)
+    Nc = vbs.size
+    idx = _random_topk(1, 2, Nc, 5)
+    perm = np.array([[[RNG.permutation(row) for row in head] for head in b] for b in idx])
+    a = oracle.fwd(q, k, v, idx, vbs)
+    b = oracle.fwd(q, k, v, perm.astype(np.int32), vbs)
+    np.testing.assert_allclose(b, a, rtol=1e-14, atol=1e-15)
+
+
+def test_fwd_convex_hull_of_selected_values():
+    q, k, v, vbs = _tiled_case(5, 6, 7, NH=2, D=16)
+    q *= 3.0
+    idx = _random_topk(1, 2, 8, 3)
+    out = oracle.fwd(q, k, v, idx, vbs)
+    for h in range(2):
+        for c in range(8):
+            rows = np.concatenate([64 * j + np.arange(vbs[j]) for j in idx[0, h, c]])
+            lo = v[0, rows, h].min(axis=0)
+            hi = v[0, rows, h].max(axis=0)
+            o = out[0, 64 * c:64 * (c + 1), h]
+            assert np.all(o >= lo - 1e-12) and np.all(o <= hi + 1e-12)
+
+
+def test_fwd_single_token_selection_returns_that_row():
+    """topk = 1 onto a cube with vbs = 1: every row's output is that v row."""
+    T, H, W = 5, 5, 5     # last cube along each axis has extent 1 -> vbs 1 corner
+    vbs = oracle.cube_sizes(T, H, W)
+    j = int(np.where(vbs == 1)[0][0])
+    q, k, v, _ = _tiled_case(T, H, W, NH=1, D=8)
+    idx = np.full((1, 1, vbs.size, 1), j, dtype=np.int32)
+    out = oracle.fwd(q, k, v, idx, vbs)
+    np.testing.assert_array_equal(out[0, :, 0], np.broadcast_to(v[0, 64 * j, 0], out[0, :, 0].shape))
+
+
+def test_fwd_zero_query_is_mean_of_selected_values():
+    q, k, v, vbs = _tiled_case(5, 6, 7, NH=1, D=8)
+    q[:] = 0.0
+    idx = _random_topk(1, 1, 8, 3)
+    out = oracle.fwd(q, k, v, idx, vbs)
+    for c in range(8):
+        rows = np.concatenate([64 * j + np.arange(vbs[j]) for j in idx[0, 0, c]])
+        np.testing.assert_allclose(out[0, 64 * c:64 * (c + 1), 0],
+                                   np.broadcast_to(v[0, rows, 0].mean(axis=0), (64, 8)),
+                                   rtol=0, atol=1e-14)
+
+
+def test_fwd_huge_logits_finite_and_argmax():
+    """Logits of order +-2000 (exp overflows without the row max): output is
+    finite and equals the v row of the largest logit when the gap is large."""
+    q, k, v, vbs = _tiled_case(5, 6, 7, NH=1, D=8)
+    q *= 40.0
+    k *= 40.0
+    idx = _random_topk(1, 1, 8, 4)
+    out = oracle.fwd(q, k, v, idx, vbs)
+    assert np.all(np.isfinite(out))
+    checked = 0
+    for c in range(8):
+        rows = np.concatenate([64 * j + np.arange(vbs[j]) for j in idx[0, 0, c]])
+        s = q[0, 64 * c:64 * (c + 1), 0] @ k[0, rows, 0].T / math.sqrt(8)
+        assert np.abs(s).max() > 500
+        srt = np.sort(s, axis=1)
+        for r in range(64):
+            if srt[r, -1] - srt[r, -2] > 50:
+                np.testing.assert_allclose(out[0, 64 * c + r, 0], v[0, rows[np.argmax(s[r])], 0],
+                                           rtol=0, atol=1e-15)
+                checked += 1
+    assert checked > 100
+
+
+def test_fwd_no_real_token_row_is_zero():
+    q, k, v, vbs = _tiled_case(5, 6, 7, NH=1, D=8)
+    vbs = vbs.copy()
+    vbs[3] = 0
+    idx = np.zeros((1, 1, 8, 1), dtype=np.int32)
+    idx[..., 0] = 3
+    out = oracle.fwd(q, k, v, idx, vbs)
+    assert np.all(out == 0)
+
+
+# ---------------------------------------------------------------- selector
+
+def test_mean_pool_closed_forms_and_padding_excluded():
+    T, H, W = 5, 6, 7
+    vbs = oracle.cube_sizes(T, H, W)
+    x = np.full((1, 8 * 64, 2, 4), 1e30)          # padding poisoned
+    means = RNG.standard_normal((8, 2, 4))
+    for c in range(8):
+        n = int(vbs[c])
+        # arithmetic progression around the mean: exact mean by symmetry
+        offs = (np.arange(n) - (n - 1) / 2.0)[:, None, None] * 0.25
+        x[0, 64 * c:64 * c + n] = means[c][None] + offs
+    got = oracle.mean_pool(x, vbs)
+    np.testing.assert_allclose(got[0], np.transpose(means, (1, 0, 2)), rtol=0, atol=1e-14)
+    const = np.full((1, 8 * 64, 1, 3), 0.7)
+    np.testing.assert_allclose(oracle.mean_pool(const, vbs), 0.7, rtol=0, atol=1e-15)
+
+
+def test_cube_scores_constructed_ranking():
+    """Orthonormal Kc and Qc = sum_j a_j Kc_j give scores exactly a (rotation
+    of a known coefficient vector), so the ranking is known by construction."""
+    n, D = 6, 6
+    Qm, _ = np.linalg.qr(RNG.standard_normal((D, D)))
+    Kc = Qm.T[None, None]                          # rows orthonormal
+    a = RNG.standard_normal((1, 1, 3, n))
+    Qc = a @ Kc[0, 0]
+    S = oracle.cube_scores(Qc, Kc)
+    np.testing.assert_allclose(S, a, rtol=0, atol=1e-13)
+    idx = oracle.topk_select(S, 3)
+    np.testing.assert_array_equal(idx[0, 0], np.argsort(-a[0, 0], axis=1)[:, :3])
+
+
+def _rank_count_topk(row, k):
+    """Brute force: id j's rank = #{i: s_i > s_j} + #{i < j: s_i == s_j}."""
+    n = row.size
+    out = np.empty(k, dtype=np.int64)
+    for j in range(n):
+        r = sum(1 for i in range(n) if row[i] > row[j] or (row[i] == row[j] and i < j))
+        if r < k:
+            out[r] = j
+    return out
+
+
+def test_topk_matches_rank_counting_with_ties():
+    S = RNG.integers(-3, 4, size=(1, 2, 12, 17)).astype(np.float64)   # many ties
+    for k in (1, 5, 17):
+        idx = oracle.topk_select(S, k)
+        for h in range(2):
+            for i in range(12):
+                np.testing.assert_array_equal(idx[0, h, i], _rank_count_topk(S[0, h, i], k))
+
+
+def test_topk_all_is_permutation_and_descending():
+    S = RNG.standard_normal((2, 3, 9, 9))
+    idx = oracle.topk_select(S, 9)
+    for row_ids, row in zip(idx.reshape(-1, 9), S.reshape(-1, 9)):
+        assert sorted(row_ids.tolist()) == list(range(9))
+        assert np.all(np.diff(row[row_ids]) <= 0)
+
+
+def test_select_end_to_end_tiny():
+    """Selector output fed to the fine stage reproduces the brute-force dense
+    masked attention built from the same selection (tiny grid)."""
+    T, H, W = 5, 6, 7
+    qn, kn, vn = (_randn(1, T * H * W, 2, 16) for _ in range(3))
+    qt, vbs = oracle.tile(qn, T, H, W)
+    kt, _ = oracle.tile(kn, T, H, W)
+    vt, _ = oracle.tile(vn, T, H, W)
+    idx, S = oracle.select(qt, kt, vbs, 3)
+    # the selection is the top-3 of brute-force per-cube means dotted together
+    for h in range(2):
+        for i in range(8):
+            qm = qn[0, oracle.slot_tokens(T, H, W)[i][:vbs[i]], h].mean(axis=0)
+            sc = [qm @ kn[0, oracle.slot_tokens(T, H, W)[j][:vbs[j]], h].mean(axis=0)
+                  for j in range(8)]
+            np.testing.assert_array_equal(idx[0, h, i], _rank_count_topk(np.array(sc), 3))
+    got = oracle.fwd(qt, kt, vt, idx, vbs)
+    np.testing.assert_allclose(got, _dense_masked(qt, kt, vt, idx, vbs, 0.25), rtol=0, atol=1e-12)
+
+
+def test_fwd_rejects_bad_indices():
+    q, k, v, vbs = _tiled_case(5, 6, 7, NH=1, D=8)
+    idx = np.zeros((1, 1, 8, 2), dtype=np.int32)      # duplicate id 0
+    with pytest.raises(AssertionError):
+        oracle.fwd(q, k, v, idx, vbs)
+    idx[..., 1] = 8                                     # out of range
+    with pytest.raises(AssertionError):
+        oracle.fwd(q, k, v, idx, vbs)
