@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the VSA hot path on one MI355X.
+
+A step is one pass of the whole path over the Wan2.2-A14B-shaped input
+(q, k, v (1, 39936, 40, 128) bf16 after tiling; grid 21x30x52; 624 cubes):
+  tile(q), tile(k), tile(v) -> select (pool, scores, top-78) -> fwd -> untile(out).
+Inputs are resident in HBM before timing. Each kernel group is bracketed by
+events on the stream the library launches on (torch's current stream).
+
+The headline figure is the fine forward (vsa_fwd): kernel-only, warmed,
+effective TFLOP/s = 4 * D * 64 * sum over (b, h, query cube) of the real
+tokens of the selected cubes, divided by its mean launch time. The same
+kernel is also timed at topk = all (dense). The CPU oracle is timed on a
+bounded sample of the same workload as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+
+
+def fwd_flops(topk_idx: np.ndarray, vbs: np.ndarray, D: int) -> float:
+    """4 * D * (64 query rows) * (real selected KV tokens), summed over units."""
+    sel_tokens = vbs[topk_idx].astype(np.int64).sum()
+    return 4.0 * D * 64.0 * float(sel_tokens)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--fwd-reps", type=int, default=50,
+                    help="extra back-to-back vsa_fwd launches timed for the kernel figure")
+    ap.add_argument("--sweep", action="store_true", help="also time topk in {624,312,187,78,31}")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time only vsa_fwd launches (for profiler runs)")
+    return ap.parse_args()
+
+
+def cpu_baseline(case, seconds: float) -> dict:
+    """Time the CPU oracle (as it stands) on whole heads of the workload until
+    about `seconds` of work; report effective TFLOP/s in the metric's unit."""
+    import threadpoolctl
+
+    import oracle
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    done_units, flops, spent = 0, 0.0, 0.0
+    heads_used = 0
+    for h in range(case.NH):
+        q_t, vbs = oracle.tile(case.q[:, :, h:h + 1], case.T, case.H, case.W)
+        k_t, _ = oracle.tile(case.k[:, :, h:h + 1], case.T, case.H, case.W)
+        v_t, _ = oracle.tile(case.v[:, :, h:h + 1], case.T, case.H, case.W)
+        q64, k64, v64 = (oracle.decode_bf16(a) for a in (q_t, k_t, v_t))
+        idx, _ = oracle.select(q64, k64, vbs, case.topk)
+        heads_used += 1
+        for c in range(vbs.size):
+            t0 = time.perf_counter()
+            oracle.fwd_unit(q64, k64, v64, idx, vbs, 0, 0, c)
+            spent += time.perf_counter() - t0
+            flops += fwd_flops(idx[0, 0, c:c + 1], vbs, case.D)
+            done_units += 1
+            if spent >= seconds:
+                break
+        if spent >= seconds:
+            break
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle fwd on {done_units} of {case.NH * 624} "
+                   f"(head, query-cube) units of the Wan workload ({heads_used} head(s), "
+                   f"oracle-selected top-{case.topk}); {spent:.1f} s of fwd time, "
+                   f"host cores visible {len(os.sched_getaffinity(0))}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the VSA path here runs on a single MI355X; "
+              "multi-GPU runs are not part of this build (see the sharding notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import video_dit_block_amd as vsa
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    print("[bench] generating the Wan-shaped input (seed 2)", file=sys.stderr, flush=True)
+    case = synth.wan()
+    T, H, W, NH, D, B, topk = case.T, case.H, case.W, case.NH, case.D, case.B, case.topk
+    to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_gpu(case.q), to_gpu(case.k), to_gpu(case.v)
+    Nc = vsa.num_cubes(T, H, W)
+    S = Nc * 64
+    qt, kt, vt = (torch.empty((B, S, NH, D), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    vbs = torch.empty(Nc, dtype=torch.int32, device=dev)
+    ws = torch.empty(vsa.select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=dev)
+    out = torch.empty_like(qt)
+    out_nat = torch.empty_like(q)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = [ev() for _ in range(5)]
+
+    def step(record: bool):
+        if record:
+            marks[0].record()
+        vsa.tile(q, T, H, W, out=qt, vbs=vbs)
+        vsa.tile(k, T, H, W, out=kt, vbs=vbs)
+        vsa.tile(v, T, H, W, out=vt, vbs=vbs)
+        if record:
+            marks[1].record()
+        vsa.select(qt, kt, vbs, topk, workspace=ws, out=idx)
+        if record:
+            marks[2].record()
+        vsa.fwd(qt, kt, vt, idx, vbs, out=out)
+        if record:
+            marks[3].record()
+        vsa.untile(out, T, H, W, out=out_nat)
+        if record:
+            marks[4].record()
+
+    if args.fwd_only:
+        step(False)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup + args.steps):
+            vsa.fwd(qt, kt, vt, idx, vbs, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"fwd_only": True, "launches": args.warmup + args.steps}))
+        return
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    parts = np.zeros(4)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        parts += [marks[i].elapsed_time(marks[i + 1]) for i in range(4)]
+    wall = (time.perf_counter() - t0) / args.steps * 1e3
+    parts /= args.steps
+    step_ms = float(parts.sum())
+
+    # the fine forward alone, back to back (kernel-only, warmed)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(args.fwd_reps):
+        vsa.fwd(qt, kt, vt, idx, vbs, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / args.fwd_reps
+
+    vbs_h = vbs.cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    flops = fwd_flops(idx_h, vbs_h, D)
+    tflops = flops / (fwd_ms * 1e-3) / 1e12
+    finite = bool(torch.isfinite(out.float()).all())
+
+    # same kernel, topk = all cubes (dense)
+    idx_all = torch.empty((B, NH, Nc, Nc), dtype=torch.int32, device=dev)
+    vsa.select(qt, kt, vbs, Nc, workspace=ws, out=idx_all)
+    out_d = torch.empty_like(qt)
+    vsa.fwd(qt, kt, vt, idx_all, vbs, out=out_d)
+    torch.cuda.synchronize()
+    reps_d = max(3, args.fwd_reps // 10)
+    e0.record()
+    for _ in range(reps_d):
+        vsa.fwd(qt, kt, vt, idx_all, vbs, out=out_d)
+    e1.record()
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / reps_d
+    dense_flops = fwd_flops(idx_all.cpu().numpy(), vbs_h, D)
+
+    sweep = None
+    if args.sweep:
+        sweep = {}
+        for kk in synth.SWEEP_TOPK:
+            ik = idx_all[..., :kk].contiguous()
+            vsa.fwd(qt, kt, vt, ik, vbs, out=out_d)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps_d):
+                vsa.fwd(qt, kt, vt, ik, vbs, out=out_d)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps_d
+            fl = fwd_flops(ik.cpu().numpy(), vbs_h, D)
+            sweep[str(kk)] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                              "speedup_vs_dense": round(dense_ms / ms, 3)}
+        del ik
+    del idx_all, out_d
+
+    # tiling traffic: read real rows, write all rows, per tensor
+    tile_bytes = 3 * (T * H * W + S) * NH * D * 2
+    cpu = None if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
+
+    line = {
+        "metric": "fine VSA fwd kernel ms + effective TFLOP/s (% bf16 peak), Wan2.2 shape, "
+                  "87.5% sparse",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Wan2.2-A14B-shaped VSA: q,k,v (1, 39936, 40, 128) bf16 BSHD, grid "
+                        "21x30x52 -> 624 cubes, topk 78 (87.5% sparse), sm_scale 1/sqrt(128), "
+                        "heavy-tailed q/k with one +-2000-logit head, seed 2",
+            "global_batch": B, "seq_len": S, "heads": NH, "head_dim": D, "topk": topk,
+            "parallelism": "single GPU",
+        },
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflop": round(flops / 1e12, 4),
+        "fwd_pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd_finite": finite,
+        "dense": {"topk": Nc, "ms": round(dense_ms, 4), "tflop": round(dense_flops / 1e12, 3),
+                  "tflops": round(dense_flops / dense_ms / 1e9, 1),
+                  "speedup_sparse_vs_dense": round(dense_ms / fwd_ms, 3)},
+        "step_breakdown_ms": {"tile_qkv": round(parts[0], 4), "select": round(parts[1], 4),
+                              "fwd": round(parts[2], 4), "untile": round(parts[3], 4)},
+        "tile_qkv_gbs": round(tile_bytes / (parts[0] * 1e-3) / 1e9, 1),
+        "wall_ms_per_step": round(wall, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    if sweep is not None:
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

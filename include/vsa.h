@@ -1,0 +1,174 @@
+/*
+ * vsa.h -- C ABI of libvsa, the MI355X (gfx950) Video Sparse Attention hot path.
+ *
+ * The path has three stages:
+ *   1. vsa_tile    cube tiling of the (T, H, W) latent grid into 64-token
+ *                  4x4x4 cubes (cube-major, padded);
+ *   2. vsa_select  the coarse selector: mean-pool q and k per cube, score cube
+ *                  against cube, keep the top-k key cubes of every query cube;
+ *   3. vsa_fwd     the fine non-causal block-sparse attention over the selected
+ *                  cubes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers to dense row-major buffers that the
+ *   caller allocates and owns. The library never allocates, frees or keeps a
+ *   pointer past the call.
+ * - bf16 tensors are passed as raw 16-bit patterns (vsa_bf16_t).
+ * - q, k, v and out are BSHD: [B][S][NH][D], S = tokens (natural order) or
+ *   Nc*64 (tiled order). D is 64 or 128.
+ * - Every launch is asynchronous on `stream` (a hipStream_t; NULL = the
+ *   default stream). Results are ready when that stream reaches the call.
+ * - Arguments are validated on the host before anything is launched. A
+ *   failed check returns an error status and launches nothing. A failed
+ *   launch returns VSA_ERR_HIP. vsa_last_error() describes the last error of
+ *   the calling thread.
+ * - No function holds state between calls; concurrent calls on different
+ *   streams with disjoint outputs are safe.
+ *
+ * Cube numbering: Nt = ceil(T/4), Nh = ceil(H/4), Nw = ceil(W/4), Nc = Nt*Nh*Nw;
+ * cube (ct, ch, cw) has id c = (ct*Nh + ch)*Nw + cw and holds the tokens
+ * t in [4ct, 4ct+et), y in [4ch, 4ch+eh), x in [4cw, 4cw+ew) with
+ * et = min(4, T-4ct) etc.; vbs[c] = et*eh*ew real tokens occupy slots
+ * 0..vbs[c]-1 of the cube in row-major (t, y, x) order; slots vbs[c]..63 are
+ * padding.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VSA_ABI_VERSION 1
+#define VSA_CUBE 64
+
+typedef uint16_t vsa_bf16_t; /* raw bf16 bits */
+typedef void* vsa_stream_t;  /* hipStream_t; NULL = default stream */
+
+typedef enum {
+  VSA_OK = 0,
+  VSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  VSA_ERR_SHAPE = 2,       /* a size is <= 0, inconsistent, or overflows */
+  VSA_ERR_UNSUPPORTED = 3, /* D not in {64, 128}, or Nc above VSA_MAX_CUBES */
+  VSA_ERR_RANGE = 4,       /* topk outside [1, Nkv] */
+  VSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  VSA_ERR_HIP = 6          /* no device, or the HIP runtime reported an error */
+} vsa_status;
+
+/* Largest cube count vsa_select accepts (its per-row sort holds one key per
+ * cube in LDS). */
+#define VSA_MAX_CUBES 8192
+
+/* ABI version of the loaded library (VSA_ABI_VERSION it was built with). */
+int32_t vsa_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* vsa_status_string(int32_t status);
+
+/* Message describing the last error returned on the calling thread ("" if
+ * none). Valid until the next libvsa call on this thread. */
+const char* vsa_last_error(void);
+
+/* Host, pure. Number of 4x4x4 cubes of a T x H x W grid: ceil(T/4) ceil(H/4)
+ * ceil(W/4) (Wan2.2 Production Values dataset card, section "Shapes":
+ * 624 = 6 x 8 x 13 for 21 x 30 x 52). Returns -1 if a size is <= 0. */
+int32_t vsa_num_cubes(int32_t T, int32_t H, int32_t W);
+
+/* Host, pure. Writes vbs[c] = real tokens of cube c for c < vsa_num_cubes()
+ * into the HOST buffer vbs of n_vbs entries (dataset card, "Shapes": vbs is the
+ * real, non-pad token count per KV cube). Errors: VSA_ERR_NULL, VSA_ERR_SHAPE
+ * (bad grid or n_vbs too small). */
+int32_t vsa_vbs_host(int32_t T, int32_t H, int32_t W, int32_t* vbs, int32_t n_vbs);
+
+/* Cube tiling (VSA: Accelerating Video Diffusion Inference with Sparse
+ * Attention on AMD GPUs, section "Two-Stage Architecture", Stage 1: tokens are
+ * grouped into (4, 4, 4) cubes of 64 tokens; dataset card, "Shapes": the
+ * sequence is cube-major and padded, S_padded = Nc x 64).
+ *   x        [B][T*H*W][NH][D] bf16, natural row-major (t, y, x) token order
+ *   x_tiled  [B][Nc*64][NH][D] bf16 output; padding slots are written as 0
+ *   vbs      [Nc] int32 device output, or NULL to skip
+ * x and x_tiled must not overlap. Errors: VSA_ERR_NULL, VSA_ERR_SHAPE,
+ * VSA_ERR_UNSUPPORTED, VSA_ERR_HIP. */
+int32_t vsa_tile(const vsa_bf16_t* x, vsa_bf16_t* x_tiled, int32_t* vbs,
+                 int32_t B, int32_t T, int32_t H, int32_t W, int32_t NH,
+                 int32_t D, vsa_stream_t stream);
+
+/* Inverse of vsa_tile: drops the padding slots (FastVideo Sliding Tile
+ * Attention guide, section "Implementation": the tile permutation is inverted
+ * to restore the sequential video order).
+ *   y_tiled  [B][Nc*64][NH][D] bf16;  y  [B][T*H*W][NH][D] bf16 output.
+ * Errors as vsa_tile. */
+int32_t vsa_untile(const vsa_bf16_t* y_tiled, vsa_bf16_t* y, int32_t B,
+                   int32_t T, int32_t H, int32_t W, int32_t NH, int32_t D,
+                   vsa_stream_t stream);
+
+/* Bytes of device workspace vsa_select needs: pooled q and k (fp32,
+ * [B][NH][Nc][D] each) and the cube score matrix (fp32, [B][NH][Nc][Nc]).
+ * Returns 0 for invalid sizes. */
+size_t vsa_select_workspace_bytes(int32_t B, int32_t NH, int32_t Nc, int32_t D);
+
+/* Coarse selector (VSA blog, "Two-Stage Architecture", Stage 1, and section
+ * "Generating Sparsity Patterns"; Optimizing block-sparse INT8 attention and
+ * multi-expert step caching for Wan 2.2, section "Decoupling Block Selection
+ * from Sparse CUDA Kernels"):
+ *   Qc[b,h,c] = mean of q_tiled[b, 64c+u, h, :] over u < vbs[c]   (fp32)
+ *   Kc likewise from k_tiled
+ *   S[b,h,i,j] = Qc[b,h,i] . Kc[b,h,j]                           (fp32)
+ *   topk_idx[b,h,i,:] = ids of the topk largest S[b,h,i,:], score
+ *                       descending, equal scores by ascending id.
+ *   q_tiled, k_tiled  [B][Nc*64][NH][D] bf16 (padding values are ignored)
+ *   vbs               [Nc] int32 device, each in [1, 64]
+ *   topk_idx          [B][NH][Nc][topk] int32 device output
+ *   workspace         device buffer of >= vsa_select_workspace_bytes() bytes,
+ *                     256-byte aligned; contents on return are unspecified.
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED, VSA_ERR_RANGE,
+ * VSA_ERR_WORKSPACE, VSA_ERR_HIP. */
+int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                   const int32_t* vbs, int32_t B, int32_t Nc, int32_t NH,
+                   int32_t D, int32_t topk, int32_t* topk_idx, void* workspace,
+                   size_t workspace_bytes, vsa_stream_t stream);
+
+/* Fine stage: non-causal block-sparse attention (Wan2.2 Production Values
+ * dataset card, section "Operator contract"; VSA blog, "Two-Stage
+ * Architecture", Stage 2, and "Sparse Traversal"). For every (b, h, query
+ * cube c) and each of its 64 rows r (padding rows included):
+ *   out[b, 64c+r, h, :] = softmax(q . K^T * sm_scale) . V
+ * where K, V are the rows 64j + u, u < vbs[j], of every j in
+ * topk_idx[b, h, c, :]. Accumulation is fp32, the softmax is computed online
+ * with the running row maximum subtracted, the output is rounded to bf16
+ * (nearest even). A row with no real key outputs 0.
+ *   q         [B][Nq*64][NH][D] bf16, tiled order (padding rows are computed
+ *             like real rows)
+ *   k, v      [B][Nkv*64][NH][D] bf16, tiled order (padding values ignored)
+ *   topk_idx  [B][NH][Nq][topk] int32; every id in [0, Nkv), distinct per row
+ *             (a precondition; vsa_validate_topk checks it)
+ *   vbs       [Nkv] int32, each in [0, 64]
+ *   out       [B][Nq*64][NH][D] bf16 output; must not overlap the inputs
+ *   sm_scale  softmax scale; <= 0 selects 1/sqrt(D); must be finite
+ * In the dataset card's self-attention Nq = Nkv; other Nkv are accepted.
+ * All tensor pointers must be 16-byte aligned. Errors: VSA_ERR_NULL,
+ * VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED, VSA_ERR_RANGE, VSA_ERR_HIP. */
+int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                const int32_t* topk_idx, const int32_t* vbs, vsa_bf16_t* out,
+                int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                int32_t topk, float sm_scale, vsa_stream_t stream);
+
+/* Checks the vsa_fwd precondition on topk_idx on the device: counts, into
+ * *bad_count (one int32 in device memory, which the caller zeroes first), the
+ * entries that are outside [0, Nkv) or repeat an earlier id of their row
+ * (VSA blog, "Block-Sparse Encoding": the index list names each selected
+ * key/value block once). Errors: VSA_ERR_NULL, VSA_ERR_SHAPE,
+ * VSA_ERR_UNSUPPORTED, VSA_ERR_RANGE, VSA_ERR_HIP. */
+int32_t vsa_validate_topk(const int32_t* topk_idx, int32_t B, int32_t NH,
+                          int32_t Nq, int32_t Nkv, int32_t topk,
+                          int32_t* bad_count, vsa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

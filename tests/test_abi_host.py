@@ -1,0 +1,119 @@
+"""The C ABI library on a host without a GPU: it loads, exports every function
+include/vsa.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from video_dit_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "vsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(vsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert len(declared) >= 11, declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.vsa_abi_version() == 1
+    for s, name in [(0, "VSA_OK"), (1, "VSA_ERR_NULL"), (2, "VSA_ERR_SHAPE"),
+                    (3, "VSA_ERR_UNSUPPORTED"), (4, "VSA_ERR_RANGE"), (5, "VSA_ERR_WORKSPACE"),
+                    (6, "VSA_ERR_HIP")]:
+        assert lib.vsa_status_string(s).decode() == name
+    assert lib.vsa_status_string(99).decode() == "VSA_ERR_UNKNOWN"
+
+
+def test_host_cube_functions():
+    lib = _lib.load()
+    assert lib.vsa_num_cubes(21, 30, 52) == 624
+    assert lib.vsa_num_cubes(30, 48, 80) == 1920
+    assert lib.vsa_num_cubes(0, 1, 1) == -1
+    buf = (ctypes.c_int32 * 8)()
+    assert lib.vsa_vbs_host(5, 6, 7, ctypes.cast(buf, ctypes.c_void_p), 8) == 0
+    assert list(buf) == [64, 48, 32, 24, 16, 12, 8, 6]
+    assert lib.vsa_vbs_host(5, 6, 7, ctypes.cast(buf, ctypes.c_void_p), 7) == _lib.VSA_ERR_SHAPE
+    assert lib.vsa_vbs_host(5, 6, 7, None, 8) == _lib.VSA_ERR_NULL
+
+
+# Fake, never-dereferenced but 256-byte aligned "device" addresses: every call
+# below fails validation on the host before any HIP call is made.
+P = 1 << 20
+
+
+def test_tile_validation():
+    lib = _lib.load()
+    assert lib.vsa_tile(None, P, None, 1, 5, 6, 7, 2, 64, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_tile(P, P, None, 1, 0, 6, 7, 2, 64, None) == _lib.VSA_ERR_SHAPE
+    assert lib.vsa_tile(P, P, None, 0, 5, 6, 7, 2, 64, None) == _lib.VSA_ERR_SHAPE
+    assert lib.vsa_tile(P, P, None, 1, 5, 6, 7, 2, 96, None) == _lib.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_tile(P + 8, P, None, 1, 5, 6, 7, 2, 64, None) == _lib.VSA_ERR_UNSUPPORTED
+    lib.vsa_tile(P, P, None, 1, 5, 6, 7, 2, 96, None)
+    assert b"D=96" in lib.vsa_last_error()
+    assert lib.vsa_untile(P, None, 1, 5, 6, 7, 2, 64, None) == _lib.VSA_ERR_NULL
+
+
+def test_select_validation():
+    lib = _lib.load()
+    need = lib.vsa_select_workspace_bytes(1, 2, 8, 64)
+    assert need >= 2 * 1 * 2 * 8 * 64 * 4 + 1 * 2 * 8 * 8 * 4
+    assert lib.vsa_select_workspace_bytes(0, 2, 8, 64) == 0
+    args = lambda topk, ws, wsb, nc=8, d=64: (P, P, P, 1, nc, 2, d, topk, P, ws, wsb, None)
+    assert lib.vsa_select(*args(3, P, need)[:2], None, *args(3, P, need)[3:]) == _lib.VSA_ERR_NULL
+    assert lib.vsa_select(*args(0, P, need)) == _lib.VSA_ERR_RANGE
+    assert lib.vsa_select(*args(9, P, need)) == _lib.VSA_ERR_RANGE
+    assert lib.vsa_select(*args(3, P, need - 1)) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_select(*args(3, None, need)) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_select(*args(3, P + 16, need)) == _lib.VSA_ERR_WORKSPACE
+    assert lib.vsa_select(*args(3, P, need, nc=8193)) == _lib.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_select(*args(3, P, need, d=32)) == _lib.VSA_ERR_UNSUPPORTED
+
+
+def test_fwd_validation():
+    lib = _lib.load()
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, idx=P, vbs=P, out=P, B=1, Nq=8, Nkv=8, NH=2, D=64, topk=3,
+                 scale=0.0)
+        a.update(kw)
+        return lib.vsa_fwd(a["q"], a["k"], a["v"], a["idx"], a["vbs"], a["out"], a["B"], a["Nq"],
+                           a["Nkv"], a["NH"], a["D"], a["topk"], a["scale"], None)
+
+    assert call(q=None) == _lib.VSA_ERR_NULL
+    assert call(vbs=None) == _lib.VSA_ERR_NULL
+    assert call(Nq=0) == _lib.VSA_ERR_SHAPE
+    assert call(NH=-1) == _lib.VSA_ERR_SHAPE
+    assert call(D=80) == _lib.VSA_ERR_UNSUPPORTED
+    assert call(topk=0) == _lib.VSA_ERR_RANGE
+    assert call(topk=9) == _lib.VSA_ERR_RANGE
+    assert call(scale=float("nan")) == _lib.VSA_ERR_RANGE
+    assert call(out=P + 2) == _lib.VSA_ERR_UNSUPPORTED
+
+
+def test_validate_topk_validation():
+    lib = _lib.load()
+    assert lib.vsa_validate_topk(None, 1, 1, 8, 8, 3, P, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_validate_topk(P, 1, 1, 8, 0, 3, P, None) == _lib.VSA_ERR_SHAPE
+    assert lib.vsa_validate_topk(P, 1, 1, 8, 9000, 3, P, None) == _lib.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_validate_topk(P, 1, 1, 8, 8, 0, P, None) == _lib.VSA_ERR_RANGE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    import video_dit_block_amd as vsa
+    x = torch.zeros(1, 210, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        vsa.tile(x, 5, 6, 7)

@@ -1,0 +1,212 @@
+// libvsa C ABI: host-side argument validation, then asynchronous launches on
+// the caller's stream. No entry point allocates or frees device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "launch.h"
+#include "vsa.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return VSA_OK;
+}
+
+constexpr int64_t kMaxGridX = 2147483647;
+constexpr int64_t kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common checks of (B, NH, D). Rows of NH*D bf16 are moved in 16-byte chunks;
+// one cube's rows (64 * NH * D elements) are indexed with 32-bit offsets.
+int32_t check_bhd(int32_t B, int32_t NH, int32_t D) {
+  if (B <= 0 || NH <= 0 || D <= 0)
+    return fail(VSA_ERR_SHAPE, "B=%d NH=%d D=%d must be positive", B, NH, D);
+  if (D != 64 && D != 128)
+    return fail(VSA_ERR_UNSUPPORTED, "D=%d not supported (64 or 128)", D);
+  if (B > kMaxGridYZ) return fail(VSA_ERR_SHAPE, "B=%d exceeds %lld", B, (long long)kMaxGridYZ);
+  if ((int64_t)NH * D * 64 > 2147483647LL)
+    return fail(VSA_ERR_SHAPE, "NH*D*64 = %lld exceeds 2^31-1", (long long)NH * D * 64);
+  return VSA_OK;
+}
+
+int32_t check_device() {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  return VSA_OK;
+}
+
+int32_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(VSA_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int64_t num_cubes64(int32_t T, int32_t H, int32_t W) {
+  if (T <= 0 || H <= 0 || W <= 0) return -1;
+  return (int64_t)((T + 3) / 4) * ((H + 3) / 4) * ((W + 3) / 4);
+}
+
+int32_t check_grid(int32_t T, int32_t H, int32_t W, int64_t* nc) {
+  *nc = num_cubes64(T, H, W);
+  if (*nc < 0) return fail(VSA_ERR_SHAPE, "grid %dx%dx%d must be positive", T, H, W);
+  if (*nc * 4 > kMaxGridX) return fail(VSA_ERR_SHAPE, "too many cubes: %lld", (long long)*nc);
+  return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vsa_abi_version(void) { return VSA_ABI_VERSION; }
+
+const char* vsa_status_string(int32_t status) {
+  switch (status) {
+    case VSA_OK: return "VSA_OK";
+    case VSA_ERR_NULL: return "VSA_ERR_NULL";
+    case VSA_ERR_SHAPE: return "VSA_ERR_SHAPE";
+    case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED";
+    case VSA_ERR_RANGE: return "VSA_ERR_RANGE";
+    case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE";
+    case VSA_ERR_HIP: return "VSA_ERR_HIP";
+    default: return "VSA_ERR_UNKNOWN";
+  }
+}
+
+const char* vsa_last_error(void) { return g_err; }
+
+int32_t vsa_num_cubes(int32_t T, int32_t H, int32_t W) {
+  const int64_t n = num_cubes64(T, H, W);
+  return (n < 0 || n > 2147483647LL) ? -1 : (int32_t)n;
+}
+
+int32_t vsa_vbs_host(int32_t T, int32_t H, int32_t W, int32_t* vbs, int32_t n_vbs) {
+  if (vbs == nullptr) return fail(VSA_ERR_NULL, "vbs is NULL");
+  const int64_t nc = num_cubes64(T, H, W);
+  if (nc < 0) return fail(VSA_ERR_SHAPE, "grid %dx%dx%d must be positive", T, H, W);
+  if (nc > n_vbs) return fail(VSA_ERR_SHAPE, "vbs holds %d entries, %lld needed", n_vbs, (long long)nc);
+  const int Nh = (H + 3) / 4, Nw = (W + 3) / 4;
+  for (int64_t c = 0; c < nc; ++c) {
+    const int cw = (int)(c % Nw), ch = (int)((c / Nw) % Nh), ct = (int)(c / ((int64_t)Nw * Nh));
+    const int et = T - 4 * ct < 4 ? T - 4 * ct : 4;
+    const int eh = H - 4 * ch < 4 ? H - 4 * ch : 4;
+    const int ew = W - 4 * cw < 4 ? W - 4 * cw : 4;
+    vbs[c] = et * eh * ew;
+  }
+  return ok();
+}
+
+int32_t vsa_tile(const vsa_bf16_t* x, vsa_bf16_t* x_tiled, int32_t* vbs, int32_t B,
+                 int32_t T, int32_t H, int32_t W, int32_t NH, int32_t D,
+                 vsa_stream_t stream) {
+  if (x == nullptr || x_tiled == nullptr) return fail(VSA_ERR_NULL, "x or x_tiled is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  int64_t nc;
+  if ((s = check_grid(T, H, W, &nc)) != VSA_OK) return s;
+  if (!aligned16(x) || !aligned16(x_tiled))
+    return fail(VSA_ERR_UNSUPPORTED, "x and x_tiled must be 16-byte aligned");
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_tile(x, x_tiled, vbs, B, T, H, W, NH, D,
+                                   static_cast<hipStream_t>(stream)), "tile");
+}
+
+int32_t vsa_untile(const vsa_bf16_t* y_tiled, vsa_bf16_t* y, int32_t B, int32_t T,
+                   int32_t H, int32_t W, int32_t NH, int32_t D, vsa_stream_t stream) {
+  if (y_tiled == nullptr || y == nullptr) return fail(VSA_ERR_NULL, "y_tiled or y is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  int64_t nc;
+  if ((s = check_grid(T, H, W, &nc)) != VSA_OK) return s;
+  if (!aligned16(y) || !aligned16(y_tiled))
+    return fail(VSA_ERR_UNSUPPORTED, "y and y_tiled must be 16-byte aligned");
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_untile(y_tiled, y, B, T, H, W, NH, D,
+                                     static_cast<hipStream_t>(stream)), "untile");
+}
+
+size_t vsa_select_workspace_bytes(int32_t B, int32_t NH, int32_t Nc, int32_t D) {
+  if (B <= 0 || NH <= 0 || Nc <= 0 || D <= 0) return 0;
+  return vsa::select_workspace(B, NH, Nc, D).total;
+}
+
+int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                   const int32_t* vbs, int32_t B, int32_t Nc, int32_t NH, int32_t D,
+                   int32_t topk, int32_t* topk_idx, void* workspace,
+                   size_t workspace_bytes, vsa_stream_t stream) {
+  if (q_tiled == nullptr || k_tiled == nullptr || vbs == nullptr || topk_idx == nullptr)
+    return fail(VSA_ERR_NULL, "q_tiled, k_tiled, vbs or topk_idx is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  if (Nc <= 0) return fail(VSA_ERR_SHAPE, "Nc=%d must be positive", Nc);
+  if (Nc > VSA_MAX_CUBES)
+    return fail(VSA_ERR_UNSUPPORTED, "Nc=%d exceeds VSA_MAX_CUBES=%d", Nc, VSA_MAX_CUBES);
+  if ((int64_t)B * NH > kMaxGridYZ)
+    return fail(VSA_ERR_SHAPE, "B*NH=%lld exceeds %lld", (long long)B * NH, (long long)kMaxGridYZ);
+  if (topk < 1 || topk > Nc) return fail(VSA_ERR_RANGE, "topk=%d outside [1, %d]", topk, Nc);
+  if (!aligned16(q_tiled) || !aligned16(k_tiled))
+    return fail(VSA_ERR_UNSUPPORTED, "q_tiled and k_tiled must be 16-byte aligned");
+  const size_t need = vsa::select_workspace(B, NH, Nc, D).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(VSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_select(q_tiled, k_tiled, vbs, B, Nc, NH, D, topk, topk_idx,
+                                     workspace, static_cast<hipStream_t>(stream)), "select");
+}
+
+int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                const int32_t* topk_idx, const int32_t* vbs, vsa_bf16_t* out, int32_t B,
+                int32_t Nq, int32_t Nkv, int32_t NH, int32_t D, int32_t topk,
+                float sm_scale, vsa_stream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || topk_idx == nullptr ||
+      vbs == nullptr || out == nullptr)
+    return fail(VSA_ERR_NULL, "q, k, v, topk_idx, vbs or out is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  if (Nq <= 0 || Nkv <= 0) return fail(VSA_ERR_SHAPE, "Nq=%d Nkv=%d must be positive", Nq, Nkv);
+  if ((int64_t)B * NH * Nq > kMaxGridX)
+    return fail(VSA_ERR_SHAPE, "B*NH*Nq=%lld exceeds %lld", (long long)B * NH * Nq,
+                (long long)kMaxGridX);
+  if (topk < 1 || topk > Nkv) return fail(VSA_ERR_RANGE, "topk=%d outside [1, %d]", topk, Nkv);
+  if (!isfinite(sm_scale)) return fail(VSA_ERR_RANGE, "sm_scale is not finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(VSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_fwd(q, k, v, topk_idx, vbs, out, B, Nq, Nkv, NH, D, topk,
+                                  sm_scale, static_cast<hipStream_t>(stream)), "fwd");
+}
+
+int32_t vsa_validate_topk(const int32_t* topk_idx, int32_t B, int32_t NH, int32_t Nq,
+                          int32_t Nkv, int32_t topk, int32_t* bad_count,
+                          vsa_stream_t stream) {
+  if (topk_idx == nullptr || bad_count == nullptr)
+    return fail(VSA_ERR_NULL, "topk_idx or bad_count is NULL");
+  if (B <= 0 || NH <= 0 || Nq <= 0 || Nkv <= 0)
+    return fail(VSA_ERR_SHAPE, "B, NH, Nq, Nkv must be positive");
+  if (Nkv > VSA_MAX_CUBES)
+    return fail(VSA_ERR_UNSUPPORTED, "Nkv=%d exceeds VSA_MAX_CUBES=%d", Nkv, VSA_MAX_CUBES);
+  if ((int64_t)B * NH * Nq > kMaxGridX) return fail(VSA_ERR_SHAPE, "too many rows");
+  if (topk < 1) return fail(VSA_ERR_RANGE, "topk=%d must be >= 1", topk);
+  int32_t s;
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_validate_topk(topk_idx, B, NH, Nq, Nkv, topk, bad_count,
+                                            static_cast<hipStream_t>(stream)), "validate_topk");
+}
+
+}  // extern "C"

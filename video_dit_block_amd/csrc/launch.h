@@ -1,0 +1,37 @@
+// Internal launch functions of libvsa (host side). The C ABI in api.hip
+// validates arguments and then calls these; each enqueues its kernels on
+// `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vsa {
+
+hipError_t launch_tile(const uint16_t* x, uint16_t* x_tiled, int32_t* vbs, int B,
+                       int T, int H, int W, int NH, int D, hipStream_t stream);
+hipError_t launch_untile(const uint16_t* y_tiled, uint16_t* y, int B, int T,
+                         int H, int W, int NH, int D, hipStream_t stream);
+
+// Workspace carve-up of vsa_select: pooled q, pooled k, scores.
+struct SelectWorkspace {
+  size_t qc_off, kc_off, s_off, total;
+};
+SelectWorkspace select_workspace(int B, int NH, int Nc, int D);
+
+hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
+                         const int32_t* vbs, int B, int Nc, int NH, int D,
+                         int topk, int32_t* topk_idx, void* workspace,
+                         hipStream_t stream);
+
+hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int32_t* topk_idx, const int32_t* vbs, uint16_t* out,
+                      int B, int Nq, int Nkv, int NH, int D, int topk,
+                      float sm_scale, hipStream_t stream);
+
+hipError_t launch_validate_topk(const int32_t* topk_idx, int B, int NH, int Nq,
+                                int Nkv, int topk, int32_t* bad_count,
+                                hipStream_t stream);
+
+}  // namespace vsa

@@ -1,0 +1,231 @@
+// Coarse selector: cube mean-pool, cube-to-cube scores, per-row top-k.
+//
+// VSA: Accelerating Video Diffusion Inference with Sparse Attention on AMD
+// GPUs, section "Two-Stage Architecture", Stage 1 (each cube is mean-pooled,
+// cube-to-cube scores are computed, and every query cube keeps the Top-K key
+// cubes with the highest scores) and section "Generating Sparsity Patterns"
+// (pooled einsum, then top-k along the key axis, largest first). Optimizing
+// block-sparse INT8 attention and multi-expert step caching for Wan 2.2,
+// section "Decoupling Block Selection from Sparse CUDA Kernels" (mean-pooled
+// summaries scored by dot product).
+//
+// Three kernels on the caller's stream:
+//   pool_kernel   HBM-bound: one workgroup per (cube, batch, q|k); lanes own
+//                 16-byte column chunks of the token row and sum the cube's
+//                 real rows in fp32; the mean divides by vbs[c].
+//   score_kernel  fp32 MFMA (v_mfma_f32_16x16x4_f32): a 64x64 tile of
+//                 S = Qc . Kc^T per workgroup. fp32 inputs keep the ranking
+//                 accurate to fp32 rounding (bf16 inputs would perturb scores
+//                 by ~2^-9 relative and reorder near-ties).
+//   topk_kernel   one workgroup per score row: a bitonic sort of 64-bit keys
+//                 (order-preserving score bits, then the complemented cube id)
+//                 in LDS, descending; the first topk ids are written out.
+//                 Equal scores therefore come out by ascending cube id.
+#include "device.h"
+#include "launch.h"
+
+namespace vsa {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ---------------------------------------------------------------- pool
+
+constexpr int kPoolThreads = 256;
+
+// grid (Nc, B, 2): z = 0 pools q into qc, z = 1 pools k into kc.
+// Output layout [B][NH][Nc][D] fp32.
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(
+    const u32x4* __restrict__ q, const u32x4* __restrict__ k,
+    const int32_t* __restrict__ vbs, float* __restrict__ qc,
+    float* __restrict__ kc, int Nc, int NH, int D) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const u32x4* __restrict__ x = blockIdx.z == 0 ? q : k;
+  float* __restrict__ xc = blockIdx.z == 0 ? qc : kc;
+  const int cpr = NH * D / 8;  // 16-byte chunks (8 bf16) per token row
+  const int n = min(max(vbs[c], 0), kCube);  // clamped: never reads past the cube
+  const u32x4* __restrict__ base = x + ((size_t)b * Nc + c) * kCube * cpr;
+  for (int col = threadIdx.x; col < cpr; col += kPoolThreads) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int u = 0;
+    for (; u + 3 < n; u += 4) {
+      u32x4 t[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = base[(size_t)(u + i) * cpr + col];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(t[i][e] << 16);
+          acc[2 * e + 1] += __uint_as_float(t[i][e] & 0xFFFF0000u);
+        }
+    }
+    for (; u < n; ++u) {
+      const u32x4 t = base[(size_t)u * cpr + col];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(t[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(t[e] & 0xFFFF0000u);
+      }
+    }
+    const int elem = col * 8;
+    const int h = elem / D, d = elem - h * D;
+    float* dst = xc + (((size_t)b * NH + h) * Nc + c) * D + d;
+    floatx4 lo, hi;
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = n > 0 ? acc[e] / (float)n : 0.0f;
+      hi[e] = n > 0 ? acc[4 + e] / (float)n : 0.0f;
+    }
+    *reinterpret_cast<floatx4*>(dst) = lo;
+    *reinterpret_cast<floatx4*>(dst + 4) = hi;
+  }
+}
+
+// ---------------------------------------------------------------- scores
+
+constexpr int kScoreThreads = 256;  // 4 waves; wave w owns tile rows 16w..16w+15
+constexpr int kScoreTile = 64;
+
+// grid (ceil(Nc/64) [j tiles], ceil(Nc/64) [i tiles], B*NH).
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16] and B[l/16][l%16] and
+// receives D[4*(l/16) + r][l%16], r = 0..3. The contraction index is
+// assigned so that lane group g = l/16 covers d in [g*D/4, (g+1)*D/4): every
+// lane then reads D/4 contiguous floats of one Qc row and of one Kc row.
+template <int D>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(
+    const float* __restrict__ qc, const float* __restrict__ kc,
+    float* __restrict__ s, int Nc) {
+  constexpr int kSeg = D / 4;  // contraction steps per MFMA chain
+  const int bh = blockIdx.z;
+  const int i0 = blockIdx.y * kScoreTile, j0 = blockIdx.x * kScoreTile;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int r = lane % 16, g = lane / 16;
+  const float* __restrict__ qb = qc + (size_t)bh * Nc * D;
+  const float* __restrict__ kb = kc + (size_t)bh * Nc * D;
+  float* __restrict__ sb = s + (size_t)bh * Nc * Nc;
+
+  const int qi = min(i0 + 16 * wave + r, Nc - 1);
+  float a[kSeg];
+#pragma unroll
+  for (int t = 0; t < kSeg; t += 4) {
+    const floatx4 v = *reinterpret_cast<const floatx4*>(qb + (size_t)qi * D + g * kSeg + t);
+    a[t] = v[0]; a[t + 1] = v[1]; a[t + 2] = v[2]; a[t + 3] = v[3];
+  }
+#pragma unroll 1
+  for (int cb = 0; cb < kScoreTile / 16; ++cb) {
+    const int kj = min(j0 + 16 * cb + r, Nc - 1);
+    float bv[kSeg];
+#pragma unroll
+    for (int t = 0; t < kSeg; t += 4) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(kb + (size_t)kj * D + g * kSeg + t);
+      bv[t] = v[0]; bv[t + 1] = v[1]; bv[t + 2] = v[2]; bv[t + 3] = v[3];
+    }
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kSeg; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], bv[t], acc, 0, 0, 0);
+    const int col = j0 + 16 * cb + r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = i0 + 16 * wave + 4 * g + e;
+      if (row < Nc && col < Nc) sb[(size_t)row * Nc + col] = acc[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k
+
+constexpr int kTopkThreads = 256;
+
+// Order-preserving map of a float to u32 (larger float -> larger key); -0 is
+// folded onto +0 so that equal scores compare equal.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// grid (Nc rows, B*NH). Dynamic LDS: n_pow2 * 8 bytes.
+// Key = order_key(score) << 32 | (0xFFFFFFFF - j). Real keys are > 0; the
+// padding keys (0) sort below every real key.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    const float* __restrict__ s, int32_t* __restrict__ topk_idx, int Nc,
+    int n_pow2, int topk) {
+  extern __shared__ uint64_t keys[];
+  const size_t row = (size_t)blockIdx.y * Nc + blockIdx.x;
+  const float* __restrict__ srow = s + row * Nc;
+  for (int j = threadIdx.x; j < n_pow2; j += kTopkThreads)
+    keys[j] = j < Nc ? ((uint64_t)order_key(srow[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j)
+                     : 0ull;
+  const int half = n_pow2 / 2;
+  for (int size = 2; size <= n_pow2; size <<= 1) {
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int t = threadIdx.x; t < half; t += kTopkThreads) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const uint64_t a = keys[lo], b = keys[hi];
+        // descending within blocks whose `size` bit is clear, ascending
+        // otherwise; the last merge (size == n_pow2) is all descending
+        const bool desc = (lo & size) == 0;
+        if (desc ? (a < b) : (a > b)) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  int32_t* __restrict__ out = topk_idx + row * topk;
+  for (int t = threadIdx.x; t < topk; t += kTopkThreads)
+    out[t] = (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull));
+}
+
+}  // namespace
+
+SelectWorkspace select_workspace(int B, int NH, int Nc, int D) {
+  SelectWorkspace w;
+  const size_t pooled = (size_t)B * NH * Nc * D * sizeof(float);
+  w.qc_off = 0;
+  w.kc_off = align_up(pooled);
+  w.s_off = w.kc_off + align_up(pooled);
+  w.total = w.s_off + align_up((size_t)B * NH * Nc * Nc * sizeof(float));
+  return w;
+}
+
+hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
+                         const int32_t* vbs, int B, int Nc, int NH, int D,
+                         int topk, int32_t* topk_idx, void* workspace,
+                         hipStream_t stream) {
+  const SelectWorkspace w = select_workspace(B, NH, Nc, D);
+  char* ws = static_cast<char*>(workspace);
+  float* qc = reinterpret_cast<float*>(ws + w.qc_off);
+  float* kc = reinterpret_cast<float*>(ws + w.kc_off);
+  float* s = reinterpret_cast<float*>(ws + w.s_off);
+
+  hipLaunchKernelGGL(pool_kernel, dim3(Nc, B, 2), dim3(kPoolThreads), 0, stream,
+                     reinterpret_cast<const u32x4*>(q_tiled),
+                     reinterpret_cast<const u32x4*>(k_tiled), vbs, qc, kc, Nc, NH, D);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int nt = (Nc + kScoreTile - 1) / kScoreTile;
+  dim3 sgrid(nt, nt, B * NH);
+  if (D == 128)
+    hipLaunchKernelGGL(score_kernel<128>, sgrid, dim3(kScoreThreads), 0, stream, qc, kc, s, Nc);
+  else
+    hipLaunchKernelGGL(score_kernel<64>, sgrid, dim3(kScoreThreads), 0, stream, qc, kc, s, Nc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  int n_pow2 = 1;
+  while (n_pow2 < Nc) n_pow2 <<= 1;
+  if (n_pow2 < 2) n_pow2 = 2;
+  hipLaunchKernelGGL(topk_kernel, dim3(Nc, B * NH), dim3(kTopkThreads),
+                     (size_t)n_pow2 * sizeof(uint64_t), stream, s, topk_idx, Nc,
+                     n_pow2, topk);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

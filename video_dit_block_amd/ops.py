@@ -1,0 +1,154 @@
+"""Python binding of libvsa: argument marshalling only.
+
+Each function takes torch tensors on the GPU, checks dtypes/shapes, allocates
+outputs with torch (device memory is PyTorch's job here) and calls the C ABI
+on torch's current stream. Every step of the computation runs in libvsa's HIP
+kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+CUBE = 64
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _bf16(t: torch.Tensor, name: str, ndim: int = 4) -> None:
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != ndim:
+        raise ValueError(f"{name} must be a contiguous {ndim}-d bfloat16 CUDA tensor, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _i32(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
+
+
+def num_cubes(T: int, H: int, W: int) -> int:
+    n = _lib.load().vsa_num_cubes(T, H, W)
+    if n < 0:
+        raise ValueError(f"bad grid {T}x{H}x{W}")
+    return n
+
+
+def vbs_host(T: int, H: int, W: int) -> torch.Tensor:
+    """Real tokens per cube, computed on the host (int32 CPU tensor)."""
+    n = num_cubes(T, H, W)
+    out = torch.empty(n, dtype=torch.int32)
+    _lib.check(_lib.load().vsa_vbs_host(T, H, W, out.data_ptr(), n), "vsa_vbs_host")
+    return out
+
+
+def tile(x: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = None,
+         vbs: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """(B, T*H*W, NH, D) natural order -> ((B, Nc*64, NH, D) tiled, vbs int32 (Nc,))."""
+    _bf16(x, "x")
+    B, N, NH, D = x.shape
+    if N != T * H * W:
+        raise ValueError(f"x has {N} tokens, grid {T}x{H}x{W} has {T * H * W}")
+    nc = num_cubes(T, H, W)
+    if out is None:
+        out = torch.empty((B, nc * CUBE, NH, D), dtype=torch.bfloat16, device=x.device)
+    _bf16(out, "out")
+    if vbs is None:
+        vbs = torch.empty(nc, dtype=torch.int32, device=x.device)
+    _i32(vbs, "vbs")
+    _lib.check(_lib.load().vsa_tile(x.data_ptr(), out.data_ptr(), vbs.data_ptr(), B, T, H, W,
+                                    NH, D, _stream()), "vsa_tile")
+    return out, vbs
+
+
+def untile(y: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """(B, Nc*64, NH, D) tiled -> (B, T*H*W, NH, D) natural order."""
+    _bf16(y, "y")
+    B, S, NH, D = y.shape
+    if S != num_cubes(T, H, W) * CUBE:
+        raise ValueError("tiled length does not match the grid")
+    if out is None:
+        out = torch.empty((B, T * H * W, NH, D), dtype=torch.bfloat16, device=y.device)
+    _bf16(out, "out")
+    _lib.check(_lib.load().vsa_untile(y.data_ptr(), out.data_ptr(), B, T, H, W, NH, D,
+                                      _stream()), "vsa_untile")
+    return out
+
+
+def select_workspace_bytes(B: int, NH: int, Nc: int, D: int) -> int:
+    return int(_lib.load().vsa_select_workspace_bytes(B, NH, Nc, D))
+
+
+def select(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk: int,
+           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Coarse selector: topk_idx int32 (B, NH, Nc, topk)."""
+    _bf16(q_t, "q_t")
+    _bf16(k_t, "k_t")
+    _i32(vbs, "vbs")
+    B, S, NH, D = q_t.shape
+    Nc = S // CUBE
+    if k_t.shape != q_t.shape or S % CUBE:
+        raise ValueError("q_t and k_t must both be (B, Nc*64, NH, D)")
+    need = select_workspace_bytes(B, NH, Nc, D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_t.device)
+    if out is None:
+        out = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=q_t.device)
+    _i32(out, "out")
+    _lib.check(_lib.load().vsa_select(q_t.data_ptr(), k_t.data_ptr(), vbs.data_ptr(), B, Nc, NH,
+                                      D, topk, out.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream()),
+               "vsa_select")
+    return out
+
+
+def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch.Tensor,
+        vbs: torch.Tensor, sm_scale: float | None = None,
+        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Fine block-sparse attention: (B, Nq*64, NH, D) bf16."""
+    for t, n in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
+        _bf16(t, n)
+    _i32(topk_idx, "topk_idx")
+    _i32(vbs, "vbs")
+    B, Sq, NH, D = q_t.shape
+    Skv = k_t.shape[1]
+    if v_t.shape != k_t.shape or k_t.shape[0] != B or k_t.shape[2:] != q_t.shape[2:]:
+        raise ValueError("k_t and v_t must be (B, Nkv*64, NH, D) matching q_t")
+    if Sq % CUBE or Skv % CUBE:
+        raise ValueError("sequence lengths must be multiples of 64")
+    Nq, Nkv = Sq // CUBE, Skv // CUBE
+    if topk_idx.dim() != 4 or tuple(topk_idx.shape[:3]) != (B, NH, Nq):
+        raise ValueError(f"topk_idx must be (B, NH, Nq, topk) = ({B}, {NH}, {Nq}, k)")
+    if vbs.numel() != Nkv:
+        raise ValueError(f"vbs must hold Nkv = {Nkv} entries")
+    topk = topk_idx.shape[3]
+    if out is None:
+        out = torch.empty_like(q_t)
+    _bf16(out, "out")
+    scale = 0.0 if sm_scale is None else float(sm_scale)
+    _lib.check(_lib.load().vsa_fwd(q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(),
+                                   topk_idx.data_ptr(), vbs.data_ptr(), out.data_ptr(), B, Nq,
+                                   Nkv, NH, D, topk, scale, _stream()), "vsa_fwd")
+    return out
+
+
+def validate_topk(topk_idx: torch.Tensor, Nkv: int) -> int:
+    """Number of out-of-range or repeated ids in topk_idx (B, NH, Nq, topk)."""
+    _i32(topk_idx, "topk_idx")
+    B, NH, Nq, topk = topk_idx.shape
+    bad = torch.zeros(1, dtype=torch.int32, device=topk_idx.device)
+    _lib.check(_lib.load().vsa_validate_topk(topk_idx.data_ptr(), B, NH, Nq, Nkv, topk,
+                                             bad.data_ptr(), _stream()), "vsa_validate_topk")
+    return int(bad.item())
+
+
+def default_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)
