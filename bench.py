@@ -144,12 +144,19 @@ def main():
             marks[4].record()
 
     if args.fwd_only:
+        # profiler mode: one full step, then only vsa_fwd launches, then one
+        # plain 1 GiB device copy whose byte counts calibrate HBM counters
         step(False)
         torch.cuda.synchronize()
         for _ in range(args.warmup + args.steps):
             vsa.fwd(qt, kt, vt, idx, vbs, out=out)
         torch.cuda.synchronize()
-        print(json.dumps({"fwd_only": True, "launches": args.warmup + args.steps}))
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"fwd_only": True, "launches": args.warmup + args.steps,
+                          "calibration_copy_bytes": 1 << 30}))
         return
 
     print("[bench] warmup", file=sys.stderr, flush=True)

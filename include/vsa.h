@@ -138,9 +138,12 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
  * cube c) and each of its 64 rows r (padding rows included):
  *   out[b, 64c+r, h, :] = softmax(q . K^T * sm_scale) . V
  * where K, V are the rows 64j + u, u < vbs[j], of every j in
- * topk_idx[b, h, c, :]. Accumulation is fp32, the softmax is computed online
- * with the running row maximum subtracted, the output is rounded to bf16
- * (nearest even). A row with no real key outputs 0.
+ * topk_idx[b, h, c, :]. q.k^T runs on bf16 inputs with fp32 accumulation;
+ * the softmax is computed online in fp32 with a running row maximum
+ * subtracted; the weights and V enter the P.V product as fp16 (V is exact in
+ * fp16 for |v| <= 65504, larger magnitudes saturate to 65504) with fp32
+ * accumulation; the output is rounded to bf16 (nearest even). A row with no
+ * real key outputs 0.
  *   q         [B][Nq*64][NH][D] bf16, tiled order (padding rows are computed
  *             like real rows)
  *   k, v      [B][Nkv*64][NH][D] bf16, tiled order (padding values ignored)

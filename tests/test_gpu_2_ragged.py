@@ -69,7 +69,7 @@ def test_nq_differs_from_nkv():
 def test_huge_logits_stay_finite():
     """Logits of order +-1e3 (q, k scaled): a softmax without the row max
     overflows; the kernel's output stays finite and matches the oracle."""
-    q, k, v, vbs, idx = _case(1, 8, 8, 2, 128, 4, seed=8, scale_qk=9.0)
+    q, k, v, vbs, idx = _case(1, 8, 8, 2, 128, 4, seed=8, scale_qk=16.0)
     qs = oracle.decode_bf16(q)[0, :, 0]
     ks = oracle.decode_bf16(k)[0, :, 0]
     assert np.abs(qs[:256] @ ks[:256].T).max() / math.sqrt(128) > 500
