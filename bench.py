@@ -32,6 +32,26 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
 
+def profiled_traffic() -> float | None:
+    """HBM bytes per vsa_fwd launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated against a 1 GiB copy), or None when the
+    fine kernel's source has changed since those counters were taken."""
+    import hashlib
+
+    prof = os.path.join(ROOT, "profiles", "fwd_kernel_wan.md")
+    src = os.path.join(ROOT, "video_dit_block_amd", "csrc", "fwd.hip")
+    try:
+        fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines()
+                      if line.split(": ", 1)[0] in ("fwd_source_sha256", "fetch_bytes_per_launch",
+                                                    "write_bytes_per_launch"))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if fields.get("fwd_source_sha256") != sha:
+        return None
+    return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])
+
+
 def fwd_flops(topk_idx: np.ndarray, vbs: np.ndarray, D: int) -> float:
     """4 * D * (64 query rows) * (real selected KV tokens), summed over units."""
     sel_tokens = vbs[topk_idx].astype(np.int64).sum()
@@ -260,7 +280,7 @@ def main():
         "wall_ms_per_step": round(wall, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": profiled_traffic()},
         "cpu_baseline": cpu,
     }
     if sweep is not None:
