@@ -140,6 +140,7 @@ def main():
     vbs = torch.empty(Nc, dtype=torch.int32, device=dev)
     ws = torch.empty(vsa.select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8, device=dev)
     idx = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=dev)
+    wsf = torch.empty(vsa.fwd_workspace_bytes(B, Nc, NH, D), dtype=torch.uint8, device=dev)
     out = torch.empty_like(qt)
     out_nat = torch.empty_like(q)
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -156,7 +157,7 @@ def main():
         vsa.select(qt, kt, vbs, topk, workspace=ws, out=idx)
         if record:
             marks[2].record()
-        vsa.fwd(qt, kt, vt, idx, vbs, out=out)
+        vsa.fwd(qt, kt, vt, idx, vbs, out=out, workspace=wsf)
         if record:
             marks[3].record()
         vsa.untile(out, T, H, W, out=out_nat)
@@ -169,7 +170,7 @@ def main():
         step(False)
         torch.cuda.synchronize()
         for _ in range(args.warmup + args.steps):
-            vsa.fwd(qt, kt, vt, idx, vbs, out=out)
+            vsa.fwd(qt, kt, vt, idx, vbs, out=out, workspace=wsf)
         torch.cuda.synchronize()
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -197,7 +198,7 @@ def main():
     e0, e1 = ev(), ev()
     e0.record()
     for _ in range(args.fwd_reps):
-        vsa.fwd(qt, kt, vt, idx, vbs, out=out)
+        vsa.fwd(qt, kt, vt, idx, vbs, out=out, workspace=wsf)
     e1.record()
     torch.cuda.synchronize()
     fwd_ms = e0.elapsed_time(e1) / args.fwd_reps
@@ -212,12 +213,12 @@ def main():
     idx_all = torch.empty((B, NH, Nc, Nc), dtype=torch.int32, device=dev)
     vsa.select(qt, kt, vbs, Nc, workspace=ws, out=idx_all)
     out_d = torch.empty_like(qt)
-    vsa.fwd(qt, kt, vt, idx_all, vbs, out=out_d)
+    vsa.fwd(qt, kt, vt, idx_all, vbs, out=out_d, workspace=wsf)
     torch.cuda.synchronize()
     reps_d = max(3, args.fwd_reps // 10)
     e0.record()
     for _ in range(reps_d):
-        vsa.fwd(qt, kt, vt, idx_all, vbs, out=out_d)
+        vsa.fwd(qt, kt, vt, idx_all, vbs, out=out_d, workspace=wsf)
     e1.record()
     torch.cuda.synchronize()
     dense_ms = e0.elapsed_time(e1) / reps_d
@@ -228,11 +229,11 @@ def main():
         sweep = {}
         for kk in synth.SWEEP_TOPK:
             ik = idx_all[..., :kk].contiguous()
-            vsa.fwd(qt, kt, vt, ik, vbs, out=out_d)
+            vsa.fwd(qt, kt, vt, ik, vbs, out=out_d, workspace=wsf)
             torch.cuda.synchronize()
             e0.record()
             for _ in range(reps_d):
-                vsa.fwd(qt, kt, vt, ik, vbs, out=out_d)
+                vsa.fwd(qt, kt, vt, ik, vbs, out=out_d, workspace=wsf)
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps_d

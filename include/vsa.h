@@ -132,6 +132,10 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                    int32_t D, int32_t topk, int32_t* topk_idx, void* workspace,
                    size_t workspace_bytes, vsa_stream_t stream);
 
+/* Bytes of device workspace vsa_fwd needs: an fp16 copy of v in the tiled
+ * layout, B * Nkv * 64 * NH * D * 2. Returns 0 for invalid sizes. */
+size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nkv, int32_t NH, int32_t D);
+
 /* Fine stage: non-causal block-sparse attention (Wan2.2 Production Values
  * dataset card, section "Operator contract"; VSA blog, "Two-Stage
  * Architecture", Stage 2, and "Sparse Traversal"). For every (b, h, query
@@ -152,13 +156,18 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
  *   vbs       [Nkv] int32, each in [0, 64]
  *   out       [B][Nq*64][NH][D] bf16 output; must not overlap the inputs
  *   sm_scale  softmax scale; <= 0 selects 1/sqrt(D); must be finite
+ *   workspace device buffer of >= vsa_fwd_workspace_bytes() bytes, 256-byte
+ *             aligned, not overlapping the tensors; contents on return are
+ *             unspecified (it holds the fp16 copy of v)
  * In the dataset card's self-attention Nq = Nkv; other Nkv are accepted.
  * All tensor pointers must be 16-byte aligned. Errors: VSA_ERR_NULL,
- * VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED, VSA_ERR_RANGE, VSA_ERR_HIP. */
+ * VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED, VSA_ERR_RANGE, VSA_ERR_WORKSPACE,
+ * VSA_ERR_HIP. */
 int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
                 const int32_t* topk_idx, const int32_t* vbs, vsa_bf16_t* out,
                 int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
-                int32_t topk, float sm_scale, vsa_stream_t stream);
+                int32_t topk, float sm_scale, void* workspace,
+                size_t workspace_bytes, vsa_stream_t stream);
 
 /* Checks the vsa_fwd precondition on topk_idx on the device: counts, into
  * *bad_count (one int32 in device memory, which the caller zeroes first), the

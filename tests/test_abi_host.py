@@ -85,11 +85,13 @@ def test_fwd_validation():
     lib = _lib.load()
 
     def call(**kw):
+        need = lib.vsa_fwd_workspace_bytes(1, 8, 2, 64)
         a = dict(q=P, k=P, v=P, idx=P, vbs=P, out=P, B=1, Nq=8, Nkv=8, NH=2, D=64, topk=3,
-                 scale=0.0)
+                 scale=0.0, ws=P, wsb=need)
         a.update(kw)
         return lib.vsa_fwd(a["q"], a["k"], a["v"], a["idx"], a["vbs"], a["out"], a["B"], a["Nq"],
-                           a["Nkv"], a["NH"], a["D"], a["topk"], a["scale"], None)
+                           a["Nkv"], a["NH"], a["D"], a["topk"], a["scale"], a["ws"], a["wsb"],
+                           None)
 
     assert call(q=None) == _lib.VSA_ERR_NULL
     assert call(vbs=None) == _lib.VSA_ERR_NULL
@@ -100,6 +102,10 @@ def test_fwd_validation():
     assert call(topk=9) == _lib.VSA_ERR_RANGE
     assert call(scale=float("nan")) == _lib.VSA_ERR_RANGE
     assert call(out=P + 2) == _lib.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_fwd_workspace_bytes(1, 8, 2, 64) == 8 * 64 * 2 * 64 * 2
+    assert call(ws=None) == _lib.VSA_ERR_WORKSPACE
+    assert call(wsb=8 * 64 * 2 * 64 * 2 - 1) == _lib.VSA_ERR_WORKSPACE
+    assert call(ws=P + 128) == _lib.VSA_ERR_WORKSPACE
 
 
 def test_validate_topk_validation():

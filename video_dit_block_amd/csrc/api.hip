@@ -169,10 +169,16 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                                      workspace, static_cast<hipStream_t>(stream)), "select");
 }
 
+size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nkv, int32_t NH, int32_t D) {
+  if (B <= 0 || Nkv <= 0 || NH <= 0 || D <= 0) return 0;
+  return vsa::fwd_workspace_bytes(B, Nkv, NH, D);
+}
+
 int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
                 const int32_t* topk_idx, const int32_t* vbs, vsa_bf16_t* out, int32_t B,
                 int32_t Nq, int32_t Nkv, int32_t NH, int32_t D, int32_t topk,
-                float sm_scale, vsa_stream_t stream) {
+                float sm_scale, void* workspace, size_t workspace_bytes,
+                vsa_stream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || topk_idx == nullptr ||
       vbs == nullptr || out == nullptr)
     return fail(VSA_ERR_NULL, "q, k, v, topk_idx, vbs or out is NULL");
@@ -186,10 +192,19 @@ int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
   if (!isfinite(sm_scale)) return fail(VSA_ERR_RANGE, "sm_scale is not finite");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(VSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  if (B > kMaxGridYZ) return fail(VSA_ERR_SHAPE, "B=%d exceeds %lld", B, (long long)kMaxGridYZ);
+  if ((int64_t)Nkv * 4 > kMaxGridX) return fail(VSA_ERR_SHAPE, "Nkv=%d too large", Nkv);
+  const size_t need = vsa::fwd_workspace_bytes(B, Nkv, NH, D);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(VSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
   if ((s = check_device()) != VSA_OK) return s;
   return launched(vsa::launch_fwd(q, k, v, topk_idx, vbs, out, B, Nq, Nkv, NH, D, topk,
-                                  sm_scale, static_cast<hipStream_t>(stream)), "fwd");
+                                  sm_scale, workspace, static_cast<hipStream_t>(stream)),
+                  "fwd");
 }
 
 int32_t vsa_validate_topk(const int32_t* topk_idx, int32_t B, int32_t NH, int32_t Nq,

@@ -57,6 +57,8 @@
 //   converted exactly for |v| <= 65504 (bf16 values are a subset of fp16 in
 //   that range) and saturates to 65504 beyond it. O / l is rounded to bf16
 //   (nearest even) and stored.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -71,16 +73,34 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 template <int D>
 struct FwdShape {
-  static constexpr int kThreads = 128;              // 2 waves x 32 query rows
-  static constexpr int kChunks = D / 8;             // 16-byte chunks per row
-  static constexpr int kGroups = kThreads / kChunks;  // token groups per tile
-  static constexpr int kTokPerThread = kCube / kGroups;  // rows each thread stages
-  static constexpr int kKPitch = D + 8;             // LDS pitch of K rows (bf16)
-  static constexpr int kVPitch = kCube + 4;         // LDS pitch of V^T rows (bf16)
-  static constexpr int kQSteps = D / 16;            // k-steps of the QK^T MFMAs
-  static constexpr int kDBlocks = D / 32;           // 32-wide d blocks of O^T
-  static_assert(kCube % kGroups == 0, "tile split");
+  static constexpr int kThreads = 128;                 // 2 waves x 32 query rows
+  static constexpr int kRowBytes = 2 * D;              // one (token, head) row
+  static constexpr int kChunks = D / 8;                // 16-byte chunks per row
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;  // rows one wave-wide DMA fills
+  static constexpr int kLoadsPerWave = kCube * kRowBytes / 1024 / 2;  // per tile, per wave
+  static constexpr int kQSteps = D / 16;               // k-steps of the QK^T MFMAs
+  static constexpr int kDBlocks = D / 32;              // 32-wide d blocks of O^T
 };
+
+// XOR swizzles of the 16-byte chunk index inside an LDS row: chunk c of row r
+// lives in slot c ^ swz(r). Chosen (by an exhaustive search over linear maps
+// of the row's low 4 bits, with a 32- and a 64-bank model) so that the two
+// read patterns below are free of bank conflicts:
+//   K: 32 lanes read chunk c of rows r..r+31 (ds_read_b128);
+//   V: the transposing read, 16-lane groups reading 8 bytes of 4
+//      consecutive rows at 4 column blocks (ds_read_b64_tr_b16).
+template <int D> __device__ __forceinline__ int swz_k(int r);
+template <int D> __device__ __forceinline__ int swz_v(int r);
+template <> __device__ __forceinline__ int swz_k<128>(int r) { return r & 15; }
+template <> __device__ __forceinline__ int swz_v<128>(int r) {
+  return ((r & 1) ? 10 : 0) ^ ((r & 2) ? 4 : 0);
+}
+template <> __device__ __forceinline__ int swz_k<64>(int r) {
+  return ((r & 1) ? 1 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 2 : 0) ^ ((r & 8) ? 1 : 0);
+}
+template <> __device__ __forceinline__ int swz_v<64>(int r) {
+  return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0);
+}
 
 // Largest index row sorted in LDS; longer rows are walked in the given order.
 constexpr int kSortCap = 1024;
@@ -89,6 +109,50 @@ constexpr int kSortCap = 1024;
 // probabilities stay <= 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kBufferDword3 = 0x00020000;  // gfx9 raw buffer resource flags
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
+
+// One wave-wide 16-byte-per-lane global -> LDS load (buffer_load_dwordx4 ...
+// lds): lane L's 16 bytes land at LDS byte lds_addr + 16 L. Issued as inline
+// assembly so that the compiler does not guard every later LDS read with a
+// wait for all outstanding loads; the kernel waits explicitly (wait_vmcnt)
+// before the barrier that publishes a tile. M0 carries the LDS base; the
+// s_nop covers the M0 -> LDS-DMA hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and used nowhere else
+__device__ __forceinline__ void dma16(int32x4_t rsrc, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// gfx9 raw buffer resource: base address, stride 0, num_records bytes.
+__device__ __forceinline__ int32x4_t buffer_rsrc(const void* base, int num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  int32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane(num_bytes);
+  r[3] = kBufferDword3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(size_t)(lds_void_ptr)(p);
+}
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4_t* lds_fp16x4_ptr;
+
+// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Both halves of the wave: combines the value of lane l%32 with that of lane
 // l%32+32 (v_permlane32_swap exchanges the halves of two registers).
@@ -106,15 +170,55 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
+// ---------------------------------------------------------------------------
+// V -> fp16 pre-pass. Writes an fp16 copy of v (same tiled BSHD layout) into
+// the workspace: real rows converted, padding rows zeroed. bf16 -> f32 is
+// exact (the bf16 bits are the upper half of an f32); f32 -> f16 truncation
+// is exact for |v| <= 65504, since every such bf16 value is an fp16 value,
+// and saturates to 65504 beyond. HBM-bound: one read and one write of v.
+constexpr int kCvtThreads = 256;
+constexpr int kCvtSplit = 4;  // workgroups per cube (16 slots each)
+
+__global__ __launch_bounds__(kCvtThreads) void v_to_fp16_kernel(
+    const u32x4* __restrict__ v, u32x4* __restrict__ v16, const int32_t* __restrict__ vbs,
+    int Nkv, int cpr) {
+  const int c = blockIdx.x / kCvtSplit, part = blockIdx.x % kCvtSplit, b = blockIdx.y;
+  const int nv = min(max(vbs[c], 0), kCube);
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+#pragma unroll 1
+  for (int r = 0; r < kCube / kCvtSplit / 4; ++r) {
+    const int u = part * (kCube / kCvtSplit) + r * 4 + wave;
+    const size_t row = ((size_t)b * Nkv + c) * kCube + u;
+    const u32x4* __restrict__ src = v + row * cpr;
+    u32x4* __restrict__ dst = v16 + row * cpr;
+    if (u < nv) {
+      for (int col = lane; col < cpr; col += 64) {
+        const u32x4 w = src[col];
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
+                                                   __uint_as_float(w[e] << 16),
+                                                   __uint_as_float(w[e] & 0xFFFF0000u)));
+        dst[col] = o;
+      }
+    } else {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      for (int col = lane; col < cpr; col += 64) dst[col] = z;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ topk_idx,
+    const uint16_t* __restrict__ v16, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ vbs, uint16_t* __restrict__ out, int Nq,
     int Nkv, int NH, int topk, float scale_log2, int n_units) {
   using S = FwdShape<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kCube * S::kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * S::kVPitch];
+  __shared__ __attribute__((aligned(1024))) uint8_t ksm[kCube * S::kRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vsm[kCube * S::kRowBytes];
   __shared__ int32_t order[kSortCap];
 
   const int unit = xcd_remap(blockIdx.x, n_units);
@@ -124,8 +228,21 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   const size_t row_stride = (size_t)NH * D;  // elements between tokens
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qr = lane & 31, g = lane >> 5;
+
+  // ---- Q of this wave's 32 rows, in the B-operand layout of S^T = K Q^T:
+  // lane (column qr, k-group g) holds q[row][16 s + 8 g .. + 7].
+  bf16x8 qf[S::kQSteps];
+  {
+    const uint16_t* qrow =
+        q + ((size_t)b * Nq * kCube + (size_t)qc * kCube + 32 * wave + qr) * row_stride +
+        (size_t)h * D;
+#pragma unroll
+    for (int s = 0; s < S::kQSteps; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * g);
+  }
 
   // ---- this unit's cube ids, sorted ascending in LDS (the result does not
   // depend on the order; a common ascending sweep lets concurrently resident
@@ -161,74 +278,27 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     return __builtin_amdgcn_readfirstlane(min(max(vbs[j], 0), kCube));
   };
 
-  // ---- Q of this wave's 32 rows, in the B-operand layout of S^T = K Q^T:
-  // lane (column qr, k-group g) holds q[row][16 s + 8 g .. + 7].
-  bf16x8 qf[S::kQSteps];
-  {
-    const uint16_t* qrow =
-        q + ((size_t)b * Nq * kCube + (size_t)qc * kCube + 32 * wave + qr) * row_stride +
-        (size_t)h * D;
+  // ---- K and V tiles go global -> LDS directly (buffer_load ... lds): each
+  // wave-wide load fills 1 KiB of LDS, lane L writing bytes [16 L, 16 L + 16).
+  // The lane fetches the global chunk that the swizzle places in that slot.
+  // The buffer range ends at the cube's vbs[j] real rows, so padding rows land
+  // in LDS as zeros. Byte offsets are < 64 * NH * D * 2 <= 2^32 (host-checked).
+  const uint32_t rs2 = (uint32_t)NH * D * 2u;
+  uint32_t koff[S::kLoadsPerWave], voff[S::kLoadsPerWave];
 #pragma unroll
-    for (int s = 0; s < S::kQSteps; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * g);
+  for (int n = 0; n < S::kLoadsPerWave; ++n) {
+    const int row = (wave * S::kLoadsPerWave + n) * S::kRowsPerKiB + lane / S::kChunks;
+    const int slot = lane % S::kChunks;
+    koff[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_k<D>(row));
+    voff[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_v<D>(row));
   }
-
-  // ---- staging maps. K: chunk-fast (16 lanes cover one 256-byte row), so
-  // both the global reads and the LDS row writes are contiguous. V: token-
-  // group-fast, so the transposed LDS writes of consecutive lanes are
-  // consecutive. Each thread stages kTokPerThread rows of one chunk.
-  const int rs = NH * D;
-  const int k_ch = tid % S::kChunks, k_tg = tid / S::kChunks;
-  const int v_tg = tid % S::kGroups, v_ch = tid / S::kGroups;
-  // byte offsets: < 64 * NH * D * 2 <= 2^32 (checked by the host), so u32
-  const uint32_t rs2 = (uint32_t)rs * 2u;
-  const uint32_t k_off = (uint32_t)(k_tg * S::kTokPerThread) * rs2 + 16u * k_ch;
-  const uint32_t v_off = (uint32_t)(v_tg * S::kTokPerThread) * rs2 + 16u * v_ch;
   const size_t kv_batch = (size_t)b * Nkv * kCube;
-  u32x4 kreg[S::kTokPerThread], vreg[S::kTokPerThread];
-
-  // Raw buffer loads with the range limited to the cube's real rows: rows at
-  // or beyond vbs[j] lie outside the range and read as zeros, so padding is
-  // never read and staged as 0 without branches.
-  auto fetch = [&](int j, int nv) {
+  auto issue = [&](const uint16_t* base, uint8_t* lds, const uint32_t* off, int j, int nv) {
     const size_t cube = (kv_batch + (size_t)j * kCube) * row_stride + (size_t)h * D;
-    // wave-uniform by construction; readfirstlane keeps the descriptor scalar
-    const int bytes = __builtin_amdgcn_readfirstlane((int)((uint32_t)nv * rs2));
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(k + cube), (short)0, bytes, kBufferDword3);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(v + cube), (short)0, bytes, kBufferDword3);
+    const int32x4_t rsrc = buffer_rsrc(base + cube, (int)((uint32_t)nv * rs2));
+    const uint32_t lds0 = lds_address(lds) + (uint32_t)(wave * S::kLoadsPerWave) * 1024u;
 #pragma unroll
-    for (int i = 0; i < S::kTokPerThread; ++i) {
-      kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + i * rs2, 0, 0));
-      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off + i * rs2, 0, 0));
-    }
-  };
-
-  auto stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < S::kTokPerThread; ++i)
-      *reinterpret_cast<u32x4*>(&ks[(k_tg * S::kTokPerThread + i) * S::kKPitch + 8 * k_ch]) = kreg[i];
-    // V^T in fp16: for each of the chunk's 8 d values, the thread's
-    // kTokPerThread consecutive tokens form one contiguous run of a V^T row.
-    // bf16 -> f32 is exact (a shift or a mask); f32 -> f16 truncation is exact
-    // for every bf16 value of magnitude <= 65504 (fp16 has the wider
-    // significand) and saturates to the largest fp16 above that.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t* dst = &vt[(8 * v_ch + e) * S::kVPitch + v_tg * S::kTokPerThread];
-      auto f32 = [&](int t) {
-        const uint32_t w = vreg[t][e >> 1];
-        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-      };
-#pragma unroll
-      for (int i = 0; i < S::kTokPerThread / 4; ++i) {
-        const u32x2 w = {
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f32(4 * i), f32(4 * i + 1))),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f32(4 * i + 2), f32(4 * i + 3)))};
-        *reinterpret_cast<u32x2*>(dst + 4 * i) = w;
-      }
-    }
+    for (int n = 0; n < S::kLoadsPerWave; ++n) dma16(rsrc, off[n], lds0 + 1024u * n);
   };
 
   floatx16 oacc[S::kDBlocks];
@@ -239,39 +309,70 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   // m_ref: reference max (raw score units) the probabilities are taken
   // against; l_run: running sum of exp2((s - m_ref) * scale_log2).
   float m_ref = kNegInf, l_run = 0.0f;
+  const floatx16 zero16 = {};
+  const halfx2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
+  // The Q loads (issued before the index sort) must be complete here, so that
+  // inside the loop the only outstanding vector-memory operations are the
+  // K/V tile loads that the explicit waits below account for.
+  wait_vmcnt<0>();
   int j = cube_id(0);
   int nv = cube_len(j);
-  fetch(j, nv);
+  issue(k, ksm, koff, j, nv);
+  issue(v16, vsm, voff, j, nv);
 
 #pragma unroll 1
   for (int it = 0; it < topk; ++it) {
     const int nv_cur = nv;
-    __syncthreads();  // every wave is done reading the previous tile
-    stage();
-    __syncthreads();
-    if (it + 1 < topk) {
+    const bool more = it + 1 < topk;
+    if (more) {
       j = cube_id(it + 1);
       nv = cube_len(j);
-      fetch(j, nv);  // in flight during the MFMAs below
     }
     const bool two = nv_cur > 32;
 
-    // ---- S^T = K Q^T for the (one or two) 32-token halves; each chain
-    // starts from an inline zero accumulator
+    // ---- K of this cube has landed (this wave's loads; V may still be in
+    // flight), then every wave's loads are visible
+    wait_vmcnt<S::kLoadsPerWave>();
+    __syncthreads();
+
+    // ---- S^T = K Q^T for the (one or two) 32-token halves. The K operands
+    // are read from LDS two k-steps ahead of the MFMAs that consume them; the
+    // two halves' chains are interleaved. Each chain starts from an inline
+    // zero accumulator.
     floatx16 sacc[2];
-    const floatx16 zero16 = {};
+    auto qk = [&](auto two_c) {
+      constexpr int NT = decltype(two_c)::value ? 2 : 1;
+      const uint8_t* krow[NT];
+      int ksw[NT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt == 1 && !two) break;
-      const uint16_t* krow = &ks[(32 * tt + qr) * S::kKPitch + 8 * g];
-      sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          *reinterpret_cast<const bf16x8*>(krow), qf[0], zero16, 0, 0, 0);
+      for (int tt = 0; tt < NT; ++tt) {
+        krow[tt] = ksm + (32 * tt + qr) * S::kRowBytes;
+        ksw[tt] = swz_k<D>(32 * tt + qr);
+      }
+      bf16x8 a[3][NT];
+      auto rd = [&](int st, int slot) {
 #pragma unroll
-      for (int s = 1; s < S::kQSteps; ++s)
-        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *reinterpret_cast<const bf16x8*>(krow + 16 * s), qf[s], sacc[tt], 0, 0, 0);
-    }
+        for (int tt = 0; tt < NT; ++tt)
+          a[slot][tt] = *reinterpret_cast<const bf16x8*>(krow[tt] + 16 * ((2 * st + g) ^ ksw[tt]));
+      };
+      rd(0, 0);
+      rd(1, 1);
+#pragma unroll
+      for (int st = 0; st < S::kQSteps; ++st) {
+        if (st + 2 < S::kQSteps) rd(st + 2, (st + 2) % 3);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st % 3][tt], qf[st],
+                                                              st == 0 ? zero16 : sacc[tt], 0, 0, 0);
+      }
+    };
+    if (two)
+      qk(std::integral_constant<bool, true>{});
+    else
+      qk(std::integral_constant<bool, false>{});
+    __syncthreads();  // every wave is done reading K: prefetch the next cube's K
+    if (more) issue(k, ksm, koff, j, nv);
 
     // ---- mask tokens >= vbs (partial cubes only), tile max
     if (nv_cur < kCube) {
@@ -312,7 +413,6 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     // values (v_dot2_f32_f16 against 1.0), so numerator and denominator agree
     float rs_sum = 0.0f;
     halfx8 pb[2][2];
-    const halfx2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       if (tt == 1 && !two) break;
@@ -332,25 +432,56 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     }
     l_run += halves_sum(rs_sum);
 
-    // ---- O^T += V^T P^T; the k-slots of lane group g are tokens
-    // base+4g+{0..3} and base+8+4g+{0..3}, matching the accumulator layout.
+    // ---- V of this cube has landed (the next K may still be in flight)
+    if (more)
+      wait_vmcnt<S::kLoadsPerWave>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+
+    // ---- O^T += V^T P^T. The A operand comes from the transposing read: in
+    // each 16-lane group, lane i receives element i%4 of the 8 bytes that
+    // lane 4e + i/4 addressed, for e = 0..3. Lane (group G, s) addresses row
+    // base + 4(G/2) + s/4 at column block 32 db + 16 (G%2) + 4 (s%4), so lane
+    // l receives d = 32 db + l%32 at tokens base + 4 (l/32) + e: the k-slots
+    // of lane group g = l/32 are tokens base+4g+{0..3} and base+8+4g+{0..3},
+    // matching the accumulator layout of P. Operands are read two MFMAs
+    // ahead.
+    {
+      const int G = lane >> 4, s4 = lane & 15;
+      const int trow = 4 * (G >> 1) + (s4 >> 2);
+      const int dcol = 16 * (G & 1) + 4 * (s4 & 3);
+      auto pv = [&](auto two_c) {
+        constexpr int NT = decltype(two_c)::value ? 2 : 1;
+        constexpr int NSTEP = NT * 2 * S::kDBlocks;  // (tt, kk, db)
+        u32x4 a[3];
+        auto rd = [&](int st, int slot) {
+          const int tt = st / (2 * S::kDBlocks), kk = (st / S::kDBlocks) % 2, db = st % S::kDBlocks;
+          const int r0 = 32 * tt + 16 * kk + trow, r1 = r0 + 8;
+          const int d0 = 32 * db + dcol;
+          const uint8_t* p0 = vsm + r0 * S::kRowBytes + 16 * ((d0 >> 3) ^ swz_v<D>(r0)) + 2 * (d0 & 7);
+          const uint8_t* p1 = vsm + r1 * S::kRowBytes + 16 * ((d0 >> 3) ^ swz_v<D>(r1)) + 2 * (d0 & 7);
+          const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p0)));
+          const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p1)));
+          a[slot] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        rd(0, 0);
+        rd(1, 1);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt == 1 && !two) break;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int base = 32 * tt + 16 * kk + 4 * g;
-#pragma unroll
-        for (int db = 0; db < S::kDBlocks; ++db) {
-          const uint16_t* src = &vt[(32 * db + qr) * S::kVPitch + base];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(halfx8, w), pb[tt][kk], oacc[db], 0, 0, 0);
+        for (int st = 0; st < NSTEP; ++st) {
+          if (st + 2 < NSTEP) rd(st + 2, (st + 2) % 3);
+          const int tt = st / (2 * S::kDBlocks), kk = (st / S::kDBlocks) % 2, db = st % S::kDBlocks;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a[st % 3]),
+                                                            pb[tt][kk], oacc[db], 0, 0, 0);
         }
-      }
+      };
+      if (two)
+        pv(std::integral_constant<bool, true>{});
+      else
+        pv(std::integral_constant<bool, false>{});
     }
+    __syncthreads();  // every wave is done reading V: prefetch the next cube's V
+    if (more) issue(v16, vsm, voff, j, nv);
   }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32 db + 8 (r/4) + 4 g + r%4
@@ -370,19 +501,30 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 
 }  // namespace
 
+size_t fwd_workspace_bytes(int B, int Nkv, int NH, int D) {
+  return (size_t)B * Nkv * kCube * NH * D * 2;
+}
+
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* topk_idx, const int32_t* vbs, uint16_t* out,
                       int B, int Nq, int Nkv, int NH, int D, int topk,
-                      float sm_scale, hipStream_t stream) {
+                      float sm_scale, void* workspace, hipStream_t stream) {
+  uint16_t* v16 = static_cast<uint16_t*>(workspace);
+  const int cpr = NH * D / 8;
+  hipLaunchKernelGGL(v_to_fp16_kernel, dim3(Nkv * kCvtSplit, B), dim3(kCvtThreads), 0, stream,
+                     reinterpret_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(v16), vbs, Nkv,
+                     cpr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int n_units = B * NH * Nq;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   if (D == 128)
     hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_units), dim3(FwdShape<128>::kThreads), 0,
-                       stream, q, k, v, topk_idx, vbs, out, Nq, Nkv, NH, topk,
+                       stream, q, k, v16, topk_idx, vbs, out, Nq, Nkv, NH, topk,
                        scale_log2, n_units);
   else
     hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_units), dim3(FwdShape<64>::kThreads), 0,
-                       stream, q, k, v, topk_idx, vbs, out, Nq, Nkv, NH, topk,
+                       stream, q, k, v16, topk_idx, vbs, out, Nq, Nkv, NH, topk,
                        scale_log2, n_units);
   return hipGetLastError();
 }

@@ -25,10 +25,12 @@ hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          int topk, int32_t* topk_idx, void* workspace,
                          hipStream_t stream);
 
+// vsa_fwd workspace: an fp16 copy of v in the tiled layout.
+size_t fwd_workspace_bytes(int B, int Nkv, int NH, int D);
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* topk_idx, const int32_t* vbs, uint16_t* out,
                       int B, int Nq, int Nkv, int NH, int D, int topk,
-                      float sm_scale, hipStream_t stream);
+                      float sm_scale, void* workspace, hipStream_t stream);
 
 hipError_t launch_validate_topk(const int32_t* topk_idx, int B, int NH, int Nq,
                                 int Nkv, int topk, int32_t* bad_count,

@@ -110,9 +110,13 @@ def select(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk: int,
     return out
 
 
+def fwd_workspace_bytes(B: int, Nkv: int, NH: int, D: int) -> int:
+    return int(_lib.load().vsa_fwd_workspace_bytes(B, Nkv, NH, D))
+
+
 def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch.Tensor,
         vbs: torch.Tensor, sm_scale: float | None = None,
-        out: torch.Tensor | None = None) -> torch.Tensor:
+        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Fine block-sparse attention: (B, Nq*64, NH, D) bf16."""
     for t, n in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
         _bf16(t, n)
@@ -134,9 +138,14 @@ def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch
         out = torch.empty_like(q_t)
     _bf16(out, "out")
     scale = 0.0 if sm_scale is None else float(sm_scale)
+    if workspace is None:
+        workspace = torch.empty(fwd_workspace_bytes(B, Nkv, NH, D), dtype=torch.uint8,
+                                device=q_t.device)
     _lib.check(_lib.load().vsa_fwd(q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(),
                                    topk_idx.data_ptr(), vbs.data_ptr(), out.data_ptr(), B, Nq,
-                                   Nkv, NH, D, topk, scale, _stream()), "vsa_fwd")
+                                   Nkv, NH, D, topk, scale, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream()),
+               "vsa_fwd")
     return out
 
 
