@@ -336,41 +336,31 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     wait_vmcnt<S::kLoadsPerWave>();
     __syncthreads();
 
-    // ---- S^T = K Q^T for the (one or two) 32-token halves. The K operands
-    // are read from LDS two k-steps ahead of the MFMAs that consume them; the
-    // two halves' chains are interleaved. Each chain starts from an inline
-    // zero accumulator.
+    // ---- S^T = K Q^T, one MFMA chain per 32-token half (the second half only
+    // when the cube has more than 32 real tokens). The K operands are read
+    // from LDS two k-steps ahead of the MFMAs that consume them. Each chain
+    // starts from an inline zero accumulator. Keeping the second half an
+    // additive block (rather than a second copy of the whole computation)
+    // keeps the accumulators in the same registers on both paths.
     floatx16 sacc[2];
-    auto qk = [&](auto two_c) {
-      constexpr int NT = decltype(two_c)::value ? 2 : 1;
-      const uint8_t* krow[NT];
-      int ksw[NT];
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        krow[tt] = ksm + (32 * tt + qr) * S::kRowBytes;
-        ksw[tt] = swz_k<D>(32 * tt + qr);
-      }
-      bf16x8 a[3][NT];
-      auto rd = [&](int st, int slot) {
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-          a[slot][tt] = *reinterpret_cast<const bf16x8*>(krow[tt] + 16 * ((2 * st + g) ^ ksw[tt]));
+    auto qk_half = [&](int tt) {
+      const uint8_t* krow = ksm + (32 * tt + qr) * S::kRowBytes;
+      const int ksw = swz_k<D>(32 * tt + qr);
+      bf16x8 a[3];
+      auto rd = [&](int st) {
+        a[st % 3] = *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * st + g) ^ ksw));
       };
-      rd(0, 0);
-      rd(1, 1);
+      rd(0);
+      rd(1);
 #pragma unroll
       for (int st = 0; st < S::kQSteps; ++st) {
-        if (st + 2 < S::kQSteps) rd(st + 2, (st + 2) % 3);
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-          sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st % 3][tt], qf[st],
-                                                              st == 0 ? zero16 : sacc[tt], 0, 0, 0);
+        if (st + 2 < S::kQSteps) rd(st + 2);
+        sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st % 3], qf[st],
+                                                            st == 0 ? zero16 : sacc[tt], 0, 0, 0);
       }
     };
-    if (two)
-      qk(std::integral_constant<bool, true>{});
-    else
-      qk(std::integral_constant<bool, false>{});
+    qk_half(0);
+    if (two) qk_half(1);
     __syncthreads();  // every wave is done reading K: prefetch the next cube's K
     if (more) issue(k, ksm, koff, j, nv);
 
@@ -451,34 +441,31 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
       const int G = lane >> 4, s4 = lane & 15;
       const int trow = 4 * (G >> 1) + (s4 >> 2);
       const int dcol = 16 * (G & 1) + 4 * (s4 & 3);
-      auto pv = [&](auto two_c) {
-        constexpr int NT = decltype(two_c)::value ? 2 : 1;
-        constexpr int NSTEP = NT * 2 * S::kDBlocks;  // (tt, kk, db)
+      auto pv_half = [&](int tt) {
+        constexpr int NSTEP = 2 * S::kDBlocks;  // (kk, db)
         u32x4 a[3];
-        auto rd = [&](int st, int slot) {
-          const int tt = st / (2 * S::kDBlocks), kk = (st / S::kDBlocks) % 2, db = st % S::kDBlocks;
+        auto rd = [&](int st) {
+          const int kk = st / S::kDBlocks, db = st % S::kDBlocks;
           const int r0 = 32 * tt + 16 * kk + trow, r1 = r0 + 8;
           const int d0 = 32 * db + dcol;
           const uint8_t* p0 = vsm + r0 * S::kRowBytes + 16 * ((d0 >> 3) ^ swz_v<D>(r0)) + 2 * (d0 & 7);
           const uint8_t* p1 = vsm + r1 * S::kRowBytes + 16 * ((d0 >> 3) ^ swz_v<D>(r1)) + 2 * (d0 & 7);
           const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p0)));
           const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p1)));
-          a[slot] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          a[st % 3] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         };
-        rd(0, 0);
-        rd(1, 1);
+        rd(0);
+        rd(1);
 #pragma unroll
         for (int st = 0; st < NSTEP; ++st) {
-          if (st + 2 < NSTEP) rd(st + 2, (st + 2) % 3);
-          const int tt = st / (2 * S::kDBlocks), kk = (st / S::kDBlocks) % 2, db = st % S::kDBlocks;
+          if (st + 2 < NSTEP) rd(st + 2);
+          const int kk = st / S::kDBlocks, db = st % S::kDBlocks;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a[st % 3]),
                                                             pb[tt][kk], oacc[db], 0, 0, 0);
         }
       };
-      if (two)
-        pv(std::integral_constant<bool, true>{});
-      else
-        pv(std::integral_constant<bool, false>{});
+      pv_half(0);
+      if (two) pv_half(1);
     }
     __syncthreads();  // every wave is done reading V: prefetch the next cube's V
     if (more) issue(v16, vsm, voff, j, nv);
