@@ -17,12 +17,14 @@
 //   contiguous range: concurrently resident query cubes are spatial
 //   neighbours of one head and their selections overlap, so key/value cubes
 //   are served from that XCD's L2.
-// * Per selected cube, K (64 x D) and V (64 x D) are staged in LDS. The next
-//   cube's rows are fetched into registers (16-byte raw buffer loads) while
-//   the MFMAs run on the current one: one LDS buffer, register double-
-//   buffering. The buffer range covers only the cube's vbs[j] real rows, so
-//   the padding rows read as zeros: pad values (even NaN) never reach an
-//   MFMA, with no branch.
+// * Per selected cube, K (64 x D, bf16) and V (64 x D, fp16 copy made by a
+//   pre-pass) are staged in LDS, one buffer each, loaded global -> LDS
+//   directly (buffer_load ... lds). The two tensors form a two-stage
+//   pipeline: V of cube j streams in while QK^T of cube j runs, K of cube
+//   j+1 while PV of cube j runs, each tile's DMAs spread one per MFMA step.
+//   The buffer range covers only the cube's vbs[j] real rows, so the padding
+//   rows land as zeros: pad values (even NaN) never reach an MFMA, with no
+//   branch.
 // * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //   the A operand is a K row slice read from LDS, the B operand is the wave's
 //   Q held in registers for the whole loop. In the accumulator layout each
@@ -33,10 +35,10 @@
 //   operand in registers. The contraction index of the PV product is
 //   permuted to match the accumulator's token order (any fixed permutation
 //   of a summation index leaves the sum unchanged).
-// * V is stored transposed in LDS (V^T, d-major, fp16), so the PV A operand
-//   is two 8-byte LDS reads per lane. O^T accumulates in fp32, each lane holding
-//   D/2 values of its own query row, so the online-softmax rescale is a
-//   per-lane multiply.
+// * V is stored row-major in LDS; the PV A operand (V^T) comes from two
+//   transposing 8-byte LDS reads per lane (ds_read_b64_tr_b16). O^T
+//   accumulates in fp32, each lane holding D/2 values of its own query row,
+//   so the online-softmax rescale is a per-lane multiply.
 // * fp32 online softmax in the exp2 domain: p = exp2(s * c - m * c) with
 //   c = sm_scale * log2 e (one FMA per score), running reference max m,
 //   running sum l. The reference max is raised lazily: only when a tile's
@@ -52,7 +54,7 @@
 //   sweep the key/value cubes of their head in the same order.
 // * Precision: QK^T is a bf16 MFMA with fp32 accumulation. The PV product
 //   runs as an fp16 MFMA (v_mfma_f32_32x32x16_f16): P is rounded to fp16 and
-//   V is converted to fp16 while it is transposed into LDS. fp16 keeps 3 more
+//   V is converted to fp16 by the pre-pass. fp16 keeps 3 more
 //   significand bits than bf16, which matters for rows with few keys; V is
 //   converted exactly for |v| <= 65504 (bf16 values are a subset of fp16 in
 //   that range) and saturates to 65504 beyond it. O / l is rounded to bf16
@@ -80,6 +82,8 @@ struct FwdShape {
   static constexpr int kLoadsPerWave = kCube * kRowBytes / 1024 / 2;  // per tile, per wave
   static constexpr int kQSteps = D / 16;               // k-steps of the QK^T MFMAs
   static constexpr int kDBlocks = D / 32;              // 32-wide d blocks of O^T
+  // one tile DMA per QK k-step and per PV (16-token half, d-block) step
+  static_assert(kQSteps == kLoadsPerWave && 2 * kDBlocks == kLoadsPerWave, "DMA spread");
 };
 
 // XOR swizzles of the 16-byte chunk index inside an LDS row: chunk c of row r
@@ -293,12 +297,14 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     voff[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_v<D>(row));
   }
   const size_t kv_batch = (size_t)b * Nkv * kCube;
-  auto issue = [&](const uint16_t* base, uint8_t* lds, const uint32_t* off, int j, int nv) {
+  // Buffer resource and LDS base of one tile load; the kLoadsPerWave DMAs of
+  // a tile are spread over the MFMA loop that runs while the tile is in
+  // flight (one DMA after each MFMA step), so that no wave issues a burst of
+  // loads and stalls behind a full memory pipeline.
+  const uint32_t lds_wave = (uint32_t)(wave * S::kLoadsPerWave) * 1024u;
+  auto tile_rsrc = [&](const uint16_t* base, int j, int nv) -> int32x4_t {
     const size_t cube = (kv_batch + (size_t)j * kCube) * row_stride + (size_t)h * D;
-    const int32x4_t rsrc = buffer_rsrc(base + cube, (int)((uint32_t)nv * rs2));
-    const uint32_t lds0 = lds_address(lds) + (uint32_t)(wave * S::kLoadsPerWave) * 1024u;
-#pragma unroll
-    for (int n = 0; n < S::kLoadsPerWave; ++n) dma16(rsrc, off[n], lds0 + 1024u * n);
+    return buffer_rsrc(base + cube, (int)((uint32_t)nv * rs2));
   };
 
   floatx16 oacc[S::kDBlocks];
@@ -315,15 +321,27 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   // The Q loads (issued before the index sort) must be complete here, so that
   // inside the loop the only outstanding vector-memory operations are the
   // K/V tile loads that the explicit waits below account for.
+  //
+  // Pipeline of one cube: K(it) landed -> barrier -> QK(it), with V(it)'s
+  // DMAs issued between its MFMAs (the V buffer is free: every wave passed
+  // the barrier after PV(it-1)) -> barrier -> softmax -> V(it) landed ->
+  // barrier -> PV(it), with K(it+1)'s DMAs issued between its MFMAs (the K
+  // buffer is free: every wave passed the barrier after QK(it)). At each
+  // wait the tile about to be read is the only load in flight.
   wait_vmcnt<0>();
   int j = cube_id(0);
   int nv = cube_len(j);
-  issue(k, ksm, koff, j, nv);
-  issue(v16, vsm, voff, j, nv);
+  {
+    const int32x4_t rsrc = tile_rsrc(k, j, nv);
+    const uint32_t lds0 = lds_address(ksm) + lds_wave;
+#pragma unroll
+    for (int n = 0; n < S::kLoadsPerWave; ++n) dma16(rsrc, koff[n], lds0 + 1024u * n);
+  }
 
 #pragma unroll 1
   for (int it = 0; it < topk; ++it) {
     const int nv_cur = nv;
+    const int j_cur = j;
     const bool more = it + 1 < topk;
     if (more) {
       j = cube_id(it + 1);
@@ -331,10 +349,12 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     }
     const bool two = nv_cur > 32;
 
-    // ---- K of this cube has landed (this wave's loads; V may still be in
-    // flight), then every wave's loads are visible
-    wait_vmcnt<S::kLoadsPerWave>();
+    // ---- K of this cube has landed (this wave's loads), then every wave's
+    // loads are visible
+    wait_vmcnt<0>();
     __syncthreads();
+    const int32x4_t vrsrc = tile_rsrc(v16, j_cur, nv_cur);
+    const uint32_t vlds0 = lds_address(vsm) + lds_wave;
 
     // ---- S^T = K Q^T, one MFMA chain per 32-token half (the second half only
     // when the cube has more than 32 real tokens). The K operands are read
@@ -357,12 +377,14 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
         if (st + 2 < S::kQSteps) rd(st + 2);
         sacc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st % 3], qf[st],
                                                             st == 0 ? zero16 : sacc[tt], 0, 0, 0);
+        if (tt == 0) dma16(vrsrc, voff[st], vlds0 + 1024u * st);  // kQSteps == kLoadsPerWave
       }
     };
     qk_half(0);
     if (two) qk_half(1);
-    __syncthreads();  // every wave is done reading K: prefetch the next cube's K
-    if (more) issue(k, ksm, koff, j, nv);
+    __syncthreads();  // every wave is done reading K
+    const int32x4_t krsrc = tile_rsrc(k, j, nv);
+    const uint32_t klds0 = lds_address(ksm) + lds_wave;
 
     // ---- mask tokens >= vbs (partial cubes only), tile max
     if (nv_cur < kCube) {
@@ -422,11 +444,8 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     }
     l_run += halves_sum(rs_sum);
 
-    // ---- V of this cube has landed (the next K may still be in flight)
-    if (more)
-      wait_vmcnt<S::kLoadsPerWave>();
-    else
-      wait_vmcnt<0>();
+    // ---- V of this cube has landed, then every wave's loads are visible
+    wait_vmcnt<0>();
     __syncthreads();
 
     // ---- O^T += V^T P^T. The A operand comes from the transposing read: in
@@ -462,13 +481,13 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
           const int kk = st / S::kDBlocks, db = st % S::kDBlocks;
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a[st % 3]),
                                                             pb[tt][kk], oacc[db], 0, 0, 0);
+          // the next cube's K, one DMA per step (2 kDBlocks == kLoadsPerWave)
+          if (tt == 0 && more) dma16(krsrc, koff[st], klds0 + 1024u * st);
         }
       };
       pv_half(0);
       if (two) pv_half(1);
     }
-    __syncthreads();  // every wave is done reading V: prefetch the next cube's V
-    if (more) issue(v16, vsm, voff, j, nv);
   }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32 db + 8 (r/4) + 4 g + r%4
