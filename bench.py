@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--fwd-reps", type=int, default=50,
                     help="extra back-to-back vsa_fwd launches timed for the kernel figure")
     ap.add_argument("--sweep", action="store_true", help="also time topk in {624,312,187,78,31}")
+    ap.add_argument("--hy720", action="store_true",
+                    help="also time the whole path on the 720p HunyuanVideo-like workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--fwd-only", action="store_true",
@@ -110,6 +112,62 @@ def cpu_baseline(case, seconds: float) -> dict:
                    f"(head, query-cube) units of the Wan workload ({heads_used} head(s), "
                    f"oracle-selected top-{case.topk}); {spent:.1f} s of fwd time, "
                    f"host cores visible {len(os.sched_getaffinity(0))}"),
+    }
+
+
+def time_pipeline(case, vsa, torch, reps: int) -> dict:
+    """Event-timed tile x3 -> select -> fwd -> untile on another workload
+    (inputs resident in HBM, buffers allocated once)."""
+    dev = torch.device("cuda:0")
+    T, H, W, NH, D, B, topk = case.T, case.H, case.W, case.NH, case.D, case.B, case.topk
+    to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_gpu(case.q), to_gpu(case.k), to_gpu(case.v)
+    Nc = vsa.num_cubes(T, H, W)
+    S = Nc * 64
+    qt, kt, vt = (torch.empty((B, S, NH, D), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    vbs = torch.empty(Nc, dtype=torch.int32, device=dev)
+    ws = torch.empty(vsa.select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8, device=dev)
+    idx = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=dev)
+    wsf = torch.empty(vsa.fwd_workspace_bytes(B, Nc, NH, D), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(qt)
+    out_nat = torch.empty_like(q)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def step(record):
+        if record:
+            marks[0].record()
+        for x, xt in ((q, qt), (k, kt), (v, vt)):
+            vsa.tile(x, T, H, W, out=xt, vbs=vbs)
+        if record:
+            marks[1].record()
+        vsa.select(qt, kt, vbs, topk, workspace=ws, out=idx)
+        if record:
+            marks[2].record()
+        vsa.fwd(qt, kt, vt, idx, vbs, out=out, workspace=wsf)
+        if record:
+            marks[3].record()
+        vsa.untile(out, T, H, W, out=out_nat)
+        if record:
+            marks[4].record()
+
+    step(False)
+    torch.cuda.synchronize()
+    parts = np.zeros(4)
+    for _ in range(reps):
+        step(True)
+        torch.cuda.synchronize()
+        parts += [marks[i].elapsed_time(marks[i + 1]) for i in range(4)]
+    parts /= reps
+    flops = fwd_flops(idx.cpu().numpy(), vbs.cpu().numpy(), D)
+    return {
+        "workload": f"{case.name}: grid {T}x{H}x{W} ({T * H * W} tokens) -> {Nc} cubes, "
+                    f"{NH} heads, D {D}, topk {topk}",
+        "ms_per_step": round(float(parts.sum()), 4),
+        "step_breakdown_ms": {"tile_qkv": round(parts[0], 4), "select": round(parts[1], 4),
+                              "fwd": round(parts[2], 4), "untile": round(parts[3], 4)},
+        "fwd_tflop": round(flops / 1e12, 4),
+        "fwd_tflops": round(flops / (parts[2] * 1e-3) / 1e12, 1),
+        "fwd_finite": bool(torch.isfinite(out.float()).all()),
     }
 
 
@@ -286,6 +344,11 @@ def main():
     }
     if sweep is not None:
         line["sweep"] = sweep
+    if args.hy720:
+        del qt, kt, vt, out, out_nat, wsf, ws, idx
+        torch.cuda.empty_cache()
+        print("[bench] 720p workload", file=sys.stderr, flush=True)
+        line["hy720"] = time_pipeline(synth.hy720(), vsa, torch, reps=5)
     print(json.dumps(line), flush=True)
 
 
