@@ -128,7 +128,8 @@ def time_pipeline(case, vsa, torch, reps: int) -> dict:
     vbs = torch.empty(Nc, dtype=torch.int32, device=dev)
     ws = torch.empty(vsa.select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8, device=dev)
     idx = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=dev)
-    wsf = torch.empty(vsa.fwd_workspace_bytes(B, Nc, NH, D), dtype=torch.uint8, device=dev)
+    wsf = torch.empty(vsa.fwd_workspace_bytes(B, Nc, Nc, NH, D, topk), dtype=torch.uint8,
+                      device=dev)
     out = torch.empty_like(qt)
     out_nat = torch.empty_like(q)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -198,7 +199,9 @@ def main():
     vbs = torch.empty(Nc, dtype=torch.int32, device=dev)
     ws = torch.empty(vsa.select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8, device=dev)
     idx = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=dev)
-    wsf = torch.empty(vsa.fwd_workspace_bytes(B, Nc, NH, D), dtype=torch.uint8, device=dev)
+    # sized for topk = Nc: covers every topk of the dense run and the sweep
+    wsf = torch.empty(vsa.fwd_workspace_bytes(B, Nc, Nc, NH, D, Nc), dtype=torch.uint8,
+                      device=dev)
     out = torch.empty_like(qt)
     out_nat = torch.empty_like(q)
     ev = lambda: torch.cuda.Event(enable_timing=True)

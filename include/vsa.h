@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 1
+#define VSA_ABI_VERSION 2
 #define VSA_CUBE 64
 
 typedef uint16_t vsa_bf16_t; /* raw bf16 bits */
@@ -132,9 +132,15 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                    int32_t D, int32_t topk, int32_t* topk_idx, void* workspace,
                    size_t workspace_bytes, vsa_stream_t stream);
 
-/* Bytes of device workspace vsa_fwd needs: an fp16 copy of v in the tiled
- * layout, B * Nkv * 64 * NH * D * 2. Returns 0 for invalid sizes. */
-size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nkv, int32_t NH, int32_t D);
+/* Bytes of device workspace vsa_fwd needs for these sizes: an fp16 copy of v
+ * in the tiled layout (B * Nkv * 64 * NH * D * 2 bytes), then, per pair of
+ * neighbouring query cubes (2j, 2j+1) of one (b, h) (B * NH * ceil(Nq / 2)
+ * pairs), a schedule of the 32-token halves that hold real tokens of the
+ * cubes either query cube selected ((2 * topk + 8) steps of two uint32) and
+ * its length (one int32), each part 256-byte aligned. Returns 0 for invalid
+ * sizes. */
+size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
+                               int32_t D, int32_t topk);
 
 /* Fine stage: non-causal block-sparse attention (Wan2.2 Production Values
  * dataset card, section "Operator contract"; VSA blog, "Two-Stage
@@ -156,10 +162,12 @@ size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nkv, int32_t NH, int32_t D);
  *   vbs       [Nkv] int32, each in [0, 64]
  *   out       [B][Nq*64][NH][D] bf16 output; must not overlap the inputs
  *   sm_scale  softmax scale; <= 0 selects 1/sqrt(D); must be finite
- *   workspace device buffer of >= vsa_fwd_workspace_bytes() bytes, 256-byte
- *             aligned, not overlapping the tensors; contents on return are
- *             unspecified (it holds the fp16 copy of v)
- * In the dataset card's self-attention Nq = Nkv; other Nkv are accepted.
+ *   workspace device buffer of >= vsa_fwd_workspace_bytes(B, Nq, Nkv, NH, D,
+ *             topk) bytes, 256-byte aligned, not overlapping the tensors;
+ *             contents on return are unspecified (it holds the fp16 copy of v
+ *             and the half-tile lists)
+ * In the dataset card's self-attention Nq = Nkv; other Nkv are accepted, up
+ * to 2^24 (VSA_ERR_UNSUPPORTED beyond).
  * All tensor pointers must be 16-byte aligned. Errors: VSA_ERR_NULL,
  * VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED, VSA_ERR_RANGE, VSA_ERR_WORKSPACE,
  * VSA_ERR_HIP. */

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.vsa_abi_version() == 1
+    assert lib.vsa_abi_version() == 2
     for s, name in [(0, "VSA_OK"), (1, "VSA_ERR_NULL"), (2, "VSA_ERR_SHAPE"),
                     (3, "VSA_ERR_UNSUPPORTED"), (4, "VSA_ERR_RANGE"), (5, "VSA_ERR_WORKSPACE"),
                     (6, "VSA_ERR_HIP")]:
@@ -85,7 +85,7 @@ def test_fwd_validation():
     lib = _lib.load()
 
     def call(**kw):
-        need = lib.vsa_fwd_workspace_bytes(1, 8, 2, 64)
+        need = lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 3)
         a = dict(q=P, k=P, v=P, idx=P, vbs=P, out=P, B=1, Nq=8, Nkv=8, NH=2, D=64, topk=3,
                  scale=0.0, ws=P, wsb=need)
         a.update(kw)
@@ -102,9 +102,15 @@ def test_fwd_validation():
     assert call(topk=9) == _lib.VSA_ERR_RANGE
     assert call(scale=float("nan")) == _lib.VSA_ERR_RANGE
     assert call(out=P + 2) == _lib.VSA_ERR_UNSUPPORTED
-    assert lib.vsa_fwd_workspace_bytes(1, 8, 2, 64) == 8 * 64 * 2 * 64 * 2
+    # fp16 v (8 cubes x 64 rows x 2 heads x 64 x 2 bytes), then the step
+    # lists of the query-cube pairs (2 heads x 4 pairs x (2 * 3 + 8) steps x 8
+    # bytes -> 1024 after 256-byte rounding), then their lengths (8 int32 -> 256)
+    need = 8 * 64 * 2 * 64 * 2 + 1024 + 256
+    assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 3) == need
+    assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 0) == 0
     assert call(ws=None) == _lib.VSA_ERR_WORKSPACE
-    assert call(wsb=8 * 64 * 2 * 64 * 2 - 1) == _lib.VSA_ERR_WORKSPACE
+    assert call(wsb=need - 1) == _lib.VSA_ERR_WORKSPACE
+    assert call(Nkv=(1 << 24) + 1, topk=3) == _lib.VSA_ERR_UNSUPPORTED
     assert call(ws=P + 128) == _lib.VSA_ERR_WORKSPACE
 
 

@@ -35,7 +35,7 @@ SIGNATURES = {
     "vsa_select_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int]),
     "vsa_select": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                             _sz, _vp]),
-    "vsa_fwd_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int]),
+    "vsa_fwd_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "vsa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                          _c_int, ctypes.c_float, _vp, _sz, _vp]),
     "vsa_validate_topk": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),

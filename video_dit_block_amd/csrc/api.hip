@@ -26,6 +26,9 @@ int32_t ok() {
 
 constexpr int64_t kMaxGridX = 2147483647;
 constexpr int64_t kMaxGridYZ = 65535;
+// Largest key/value cube count of vsa_fwd: half-tile list entries hold the cube
+// id in their upper 26 bits.
+constexpr int32_t kMaxFwdCubes = 1 << 24;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -169,9 +172,10 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                                      workspace, static_cast<hipStream_t>(stream)), "select");
 }
 
-size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nkv, int32_t NH, int32_t D) {
-  if (B <= 0 || Nkv <= 0 || NH <= 0 || D <= 0) return 0;
-  return vsa::fwd_workspace_bytes(B, Nkv, NH, D);
+size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                               int32_t topk) {
+  if (B <= 0 || Nq <= 0 || Nkv <= 0 || NH <= 0 || D <= 0 || topk <= 0) return 0;
+  return vsa::fwd_workspace(B, Nq, Nkv, NH, D, topk).total;
 }
 
 int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
@@ -193,8 +197,9 @@ int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(VSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
   if (B > kMaxGridYZ) return fail(VSA_ERR_SHAPE, "B=%d exceeds %lld", B, (long long)kMaxGridYZ);
-  if ((int64_t)Nkv * 4 > kMaxGridX) return fail(VSA_ERR_SHAPE, "Nkv=%d too large", Nkv);
-  const size_t need = vsa::fwd_workspace_bytes(B, Nkv, NH, D);
+  if (Nkv > kMaxFwdCubes)
+    return fail(VSA_ERR_UNSUPPORTED, "Nkv=%d exceeds %d", Nkv, kMaxFwdCubes);
+  const size_t need = vsa::fwd_workspace(B, Nq, Nkv, NH, D, topk).total;
   if (workspace == nullptr || workspace_bytes < need)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);

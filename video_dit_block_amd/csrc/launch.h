@@ -25,8 +25,14 @@ hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          int topk, int32_t* topk_idx, void* workspace,
                          hipStream_t stream);
 
-// vsa_fwd workspace: an fp16 copy of v in the tiled layout.
-size_t fwd_workspace_bytes(int B, int Nkv, int NH, int D);
+// Workspace carve-up of vsa_fwd: an fp16 copy of v in the tiled layout, the
+// half-tile lists of the query-cube pairs ([B*NH*ceil(Nq/2)][list_stride]
+// uint32) and their lengths.
+struct FwdWorkspace {
+  size_t v16_off, list_off, count_off, total;
+  int list_stride;
+};
+FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk);
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* topk_idx, const int32_t* vbs, uint16_t* out,
                       int B, int Nq, int Nkv, int NH, int D, int topk,

@@ -110,8 +110,8 @@ def select(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk: int,
     return out
 
 
-def fwd_workspace_bytes(B: int, Nkv: int, NH: int, D: int) -> int:
-    return int(_lib.load().vsa_fwd_workspace_bytes(B, Nkv, NH, D))
+def fwd_workspace_bytes(B: int, Nq: int, Nkv: int, NH: int, D: int, topk: int) -> int:
+    return int(_lib.load().vsa_fwd_workspace_bytes(B, Nq, Nkv, NH, D, topk))
 
 
 def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch.Tensor,
@@ -139,8 +139,8 @@ def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch
     _bf16(out, "out")
     scale = 0.0 if sm_scale is None else float(sm_scale)
     if workspace is None:
-        workspace = torch.empty(fwd_workspace_bytes(B, Nkv, NH, D), dtype=torch.uint8,
-                                device=q_t.device)
+        workspace = torch.empty(fwd_workspace_bytes(B, Nq, Nkv, NH, D, topk),
+                                dtype=torch.uint8, device=q_t.device)
     _lib.check(_lib.load().vsa_fwd(q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(),
                                    topk_idx.data_ptr(), vbs.data_ptr(), out.data_ptr(), B, Nq,
                                    Nkv, NH, D, topk, scale, workspace.data_ptr(),
