@@ -133,12 +133,11 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                    size_t workspace_bytes, vsa_stream_t stream);
 
 /* Bytes of device workspace vsa_fwd needs for these sizes: an fp16 copy of v
- * in the tiled layout (B * Nkv * 64 * NH * D * 2 bytes), then, per pair of
- * neighbouring query cubes (2j, 2j+1) of one (b, h) (B * NH * ceil(Nq / 2)
- * pairs), a schedule of the 32-token halves that hold real tokens of the
- * cubes either query cube selected ((2 * topk + 8) steps of two uint32) and
- * its length (one int32), each part 256-byte aligned. Returns 0 for invalid
- * sizes. */
+ * in the tiled layout (B * Nkv * 64 * NH * D * 2 bytes), then, per (b, h,
+ * query cube) (B * NH * Nq of them), the list of the 32-token halves that
+ * hold real tokens of its selected cubes ((2 * topk + 4) entries of two
+ * uint32) and its length (one int32), each part 256-byte aligned. Returns 0
+ * for invalid sizes. */
 size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
                                int32_t D, int32_t topk);
 
@@ -166,8 +165,9 @@ size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
  *             topk) bytes, 256-byte aligned, not overlapping the tensors;
  *             contents on return are unspecified (it holds the fp16 copy of v
  *             and the half-tile lists)
- * In the dataset card's self-attention Nq = Nkv; other Nkv are accepted, up
- * to 2^24 (VSA_ERR_UNSUPPORTED beyond).
+ * In the dataset card's self-attention Nq = Nkv; other Nkv are accepted as long
+ * as one batch of k spans less than 4 GiB, Nkv * 64 * NH * D * 2 < 2^32
+ * (VSA_ERR_UNSUPPORTED beyond).
  * All tensor pointers must be 16-byte aligned. Errors: VSA_ERR_NULL,
  * VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED, VSA_ERR_RANGE, VSA_ERR_WORKSPACE,
  * VSA_ERR_HIP. */

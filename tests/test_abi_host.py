@@ -102,15 +102,17 @@ def test_fwd_validation():
     assert call(topk=9) == _lib.VSA_ERR_RANGE
     assert call(scale=float("nan")) == _lib.VSA_ERR_RANGE
     assert call(out=P + 2) == _lib.VSA_ERR_UNSUPPORTED
-    # fp16 v (8 cubes x 64 rows x 2 heads x 64 x 2 bytes), then the step
-    # lists of the query-cube pairs (2 heads x 4 pairs x (2 * 3 + 8) steps x 8
-    # bytes -> 1024 after 256-byte rounding), then their lengths (8 int32 -> 256)
-    need = 8 * 64 * 2 * 64 * 2 + 1024 + 256
+    # fp16 v (8 cubes x 64 rows x 2 heads x 64 x 2 bytes), then the half-tile
+    # lists of the 16 (head, query cube) units ((2 * 3 + 4) entries x 8 bytes
+    # each = 1280 bytes), then their lengths (16 int32 -> 256 after 256-byte
+    # rounding)
+    need = 8 * 64 * 2 * 64 * 2 + 1280 + 256
     assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 3) == need
     assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 0) == 0
     assert call(ws=None) == _lib.VSA_ERR_WORKSPACE
     assert call(wsb=need - 1) == _lib.VSA_ERR_WORKSPACE
-    assert call(Nkv=(1 << 24) + 1, topk=3) == _lib.VSA_ERR_UNSUPPORTED
+    # one batch of k must span < 4 GiB: Nkv * 64 * NH * D * 2 = Nkv * 16384 here
+    assert call(Nkv=1 << 18, topk=3) == _lib.VSA_ERR_UNSUPPORTED
     assert call(ws=P + 128) == _lib.VSA_ERR_WORKSPACE
 
 

@@ -26,9 +26,9 @@ int32_t ok() {
 
 constexpr int64_t kMaxGridX = 2147483647;
 constexpr int64_t kMaxGridYZ = 65535;
-// Largest key/value cube count of vsa_fwd: half-tile list entries hold the cube
-// id in their upper 26 bits.
-constexpr int32_t kMaxFwdCubes = 1 << 24;
+// vsa_fwd addresses a half-tile by a 32-bit byte offset from its head's first
+// key row: one batch's k (Nkv * 64 rows of NH * D bf16) must span < 4 GiB.
+constexpr uint64_t kMaxFwdKvBytes = 1ull << 32;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -197,8 +197,9 @@ int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(VSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
   if (B > kMaxGridYZ) return fail(VSA_ERR_SHAPE, "B=%d exceeds %lld", B, (long long)kMaxGridYZ);
-  if (Nkv > kMaxFwdCubes)
-    return fail(VSA_ERR_UNSUPPORTED, "Nkv=%d exceeds %d", Nkv, kMaxFwdCubes);
+  if ((uint64_t)Nkv * 64u * (uint64_t)NH * (uint64_t)D * 2u >= kMaxFwdKvBytes)
+    return fail(VSA_ERR_UNSUPPORTED, "Nkv * 64 * NH * D * 2 = %llu bytes per batch must be < 2^32",
+                (unsigned long long)Nkv * 64ull * NH * D * 2ull);
   const size_t need = vsa::fwd_workspace(B, Nq, Nkv, NH, D, topk).total;
   if (workspace == nullptr || workspace_bytes < need)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,

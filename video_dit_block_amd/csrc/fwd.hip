@@ -13,30 +13,30 @@
 // Design for gfx950
 // -----------------
 // * Two pre-passes: (1) an fp16 copy of v (the PV product runs in fp16);
-//   (2) per pair of neighbouring query cubes (2j, 2j+1) of one (b, h), the
-//   sorted union of their selected cube ids, expanded into a list of 32-token
-//   half-tiles: half 0 of every cube with a real token, half 1 of every cube
-//   with more than 32. Each entry packs the cube id, which of the two query
-//   cubes selected it, the half and its real-row count. Neighbouring query
-//   cubes select overlapping sets (about a quarter of a pair's half-tiles are
-//   shared on video workloads), and a shared half-tile is loaded once for
-//   both. The result does not depend on the order of topk_idx; the ascending
-//   sweep makes the pairs resident on one XCD walk their head's key/value
-//   cubes in the same order, which keeps them in that XCD's L2, and no half
-//   without real tokens is touched.
-// * One workgroup = one pair: 4 waves of 32 query rows (waves 0-1 the first
-//   query cube, 2-3 the second), 2 workgroups per CU. Pairs are numbered
-//   head-major and remapped so each XCD walks a contiguous range.
-// * The pair's half-tiles stream through LDS, K and V each double-buffered
-//   (2 x 2 x 8 KiB at D = 128), loaded global -> LDS directly
-//   (buffer_load ... lds), every wave loading a quarter of each half-tile:
-//   V of half-tile i+1 streams in during QK^T of half-tile i, K of half-tile
-//   i+2 during PV of half-tile i, each tile's DMAs spread one per MFMA step.
-//   That gives every load well over a half-tile's compute of lead, which the
-//   L2/MALL latency under load needs. The waves of a query cube that did not
-//   select half-tile i only issue its loads and pass the barriers. The
-//   buffer range of a load ends at the half's real rows, so padding rows land
-//   as zeros: pad values (even NaN) never reach an MFMA, with no branch.
+//   (2) per (b, h, query cube) "unit", the selected cube ids sorted ascending
+//   and expanded into a list of 32-token half-tiles: half 0 of every cube with
+//   a real token, half 1 of every cube with more than 32. Each entry holds the
+//   half-tile's byte offset from the head's first key row and its real-row
+//   count, so the fine kernel builds a load descriptor with two scalar adds
+//   and never touches a half without real tokens. The result does not depend
+//   on the order of topk_idx; the ascending sweep makes the units resident on
+//   one XCD walk their head's key/value cubes in the same order.
+// * One workgroup = one unit: 2 waves of 32 query rows, 4 workgroups per CU
+//   (2 waves per SIMD; 32 KiB of LDS each). Units are numbered head-major and
+//   remapped so each XCD walks a contiguous range.
+// * K and V half-tiles stream through LDS, each double-buffered, loaded
+//   global -> LDS directly (buffer_load ... lds, two 1 KiB loads per M0
+//   write); every wave loads half of each tile. The buffer range of a load
+//   ends at the half's real rows, so padding rows land in LDS as zeros: pad
+//   values (even NaN) never reach an MFMA.
+// * Software pipeline inside each wave (step j = half-tile j):
+//     A(j): QK^T of half-tile j+1 (8 MFMAs) interleaved with the softmax
+//           exponentials, fp16 conversion and row sums of half-tile j;
+//     B(j): PV of half-tile j (8 MFMAs) interleaved with the mask and row
+//           max of half-tile j+1.
+//   Matrix and vector work of one wave thus overlap, and the second wave on
+//   the SIMD fills the remaining gaps. Loads keep 1.5 steps of lead: A(j)
+//   issues V(j+1), B(j) issues K(j+3).
 // * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //   the A operand is a K row slice read from LDS, the B operand is the wave's
 //   Q held in registers for the whole loop. In the accumulator layout each
@@ -49,14 +49,12 @@
 //   of a summation index leaves the sum unchanged); the V^T operand comes
 //   from two transposing 8-byte LDS reads per lane (ds_read_b64_tr_b16) of
 //   row-major V.
-// * fp32 online softmax in the exp2 domain, one step per half-tile:
-//   p = exp2(s * c - m * c) with c = sm_scale * log2 e (one FMA per score),
-//   running reference max m, running sum l. The reference max is raised
-//   lazily: only when a half's row max exceeds it by more than 2^8 (log2
-//   units: 8) does the wave rescale O and l by exp2((m_old - m_new) c);
-//   otherwise p may reach 2^8, which fp32 and fp16 hold exactly in range. A
-//   fully masked row keeps m = -inf and uses 0 in the subtraction, so no
-//   (-inf) - (-inf) arises. Tokens past a half's real rows are set to -inf in
+// * fp32 online softmax in the exp2 domain: p = exp2(s * c - m * c) with
+//   c = sm_scale * log2 e (one FMA per score), reference max m, running sum
+//   l. The reference max is raised lazily: only when a half's row max
+//   exceeds it by more than 2^8 (log2 units: 8) does the wave rescale O and l
+//   by exp2((m_old - m_new) c); otherwise p may reach 2^8, which fp32 and fp16
+//   hold exactly in range. Tokens past a half's real rows are set to -inf in
 //   registers before the max (partial halves only). O^T accumulates in fp32,
 //   each lane holding D/2 values of its own query row, so the rescale is a
 //   per-lane multiply.
@@ -67,6 +65,8 @@
 //   converted exactly for |v| <= 65504 (bf16 values are a subset of fp16 in
 //   that range) and saturates to 65504 beyond it. O / l is rounded to bf16
 //   (nearest even) and stored.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -82,16 +82,15 @@ constexpr int kHalf = 32;  // tokens per half-tile
 
 template <int D>
 struct FwdShape {
-  static constexpr int kThreads = 256;                  // 2 query cubes x 2 waves x 32 rows
+  static constexpr int kThreads = 128;                  // 2 waves x 32 query rows
   static constexpr int kRowBytes = 2 * D;               // one (token, head) row
   static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
-  static constexpr int kRowsPerKiB = 1024 / kRowBytes;  // rows one wave-wide DMA fills
+  static constexpr int kRowsPerKiB = 1024 / kRowBytes;  // rows one wave-wide load fills
   static constexpr int kHalfBytes = kHalf * kRowBytes;  // one tensor of one half-tile
-  static constexpr int kLoads = kHalfBytes / 1024 / 4;  // DMAs per wave per tensor and half-tile
+  static constexpr int kLoads = kHalfBytes / 1024 / 2;  // loads per wave, tensor and half-tile
   static constexpr int kQSteps = D / 16;                // k-steps of the QK^T MFMAs
   static constexpr int kDBlocks = D / 32;               // 32-wide d blocks of O^T
-  // a half-tile's DMAs are spread over the first kLoads MFMA steps of QK / PV
-  static_assert(kLoads <= kQSteps && kLoads <= 2 * kDBlocks, "DMA spread");
+  static_assert(kLoads % 2 == 0, "loads go in pairs");
 };
 
 // XOR swizzles of the 16-byte chunk index inside an LDS row: chunk c of row r
@@ -101,6 +100,7 @@ struct FwdShape {
 //   K: 32 lanes read chunk c of rows r..r+31 (ds_read_b128);
 //   V: the transposing read, 16-lane groups reading 8 bytes of 4
 //      consecutive rows at 4 column blocks (ds_read_b64_tr_b16).
+// The V swizzle depends on the row's low 2 bits only.
 template <int D> __device__ __forceinline__ int swz_k(int r);
 template <int D> __device__ __forceinline__ int swz_v(int r);
 template <> __device__ __forceinline__ int swz_k<128>(int r) { return r & 15; }
@@ -123,32 +123,27 @@ constexpr int kBufferDword3 = 0x00020000;  // gfx9 raw buffer resource flags
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef int32_t int32x4_t __attribute__((ext_vector_type(4)));
 
-// One wave-wide 16-byte-per-lane global -> LDS load (buffer_load_dwordx4 ...
-// lds): lane L's 16 bytes land at LDS byte lds_addr + 16 L. Issued as inline
-// assembly so that the compiler does not guard every later LDS read with a
-// wait for all outstanding loads; the kernel waits explicitly (wait_vmcnt)
-// before the barrier that publishes a tile. M0 carries the LDS base; the
+// Two wave-wide 16-byte-per-lane global -> LDS loads (buffer_load_dwordx4 ...
+// lds) into consecutive KiB of LDS with one M0 write: lane L's 16 bytes of
+// the first load land at LDS byte lds_addr + 16 L, those of the second at
+// lds_addr + 1024 + 16 L. The instruction offset (1024) applies to both the
+// global and the LDS address, so the second lane offset comes pre-reduced by
+// 1024. Issued as inline assembly so that the compiler does not guard every
+// later LDS read with a wait for all outstanding loads; the kernel waits
+// explicitly (wait_vmcnt) before the barrier that publishes a tile. The
 // s_nop covers the M0 -> LDS-DMA hazard.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and used nowhere else
-__device__ __forceinline__ void dma16(int32x4_t rsrc, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+__device__ __forceinline__ void dma16x2(int32x4_t rsrc, uint32_t voff0, uint32_t voff1m,
+                                        uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+      :
+      : "s"(lds_addr), "v"(voff0), "v"(voff1m), "s"(rsrc)
+      : "memory", "m0");
 }
 #pragma clang diagnostic pop
-
-// gfx9 raw buffer resource: base address, stride 0, num_records bytes.
-__device__ __forceinline__ int32x4_t buffer_rsrc(const void* base, int num_bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  int32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
-  r[2] = __builtin_amdgcn_readfirstlane(num_bytes);
-  r[3] = kBufferDword3;
-  return r;
-}
 
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(size_t)(lds_void_ptr)(p);
@@ -179,6 +174,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 // ---------------------------------------------------------------------------
 // V -> fp16 pre-pass. Writes an fp16 copy of v (same tiled BSHD layout) into
@@ -220,52 +218,37 @@ __global__ __launch_bounds__(kCvtThreads) void v_to_fp16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Step list pre-pass: one workgroup per pair of neighbouring query cubes
-// (2j, 2j+1) of one (b, h). The two index rows are merged into their sorted
-// union, each cube expanded into its 32-token half-tiles (half 0 if it has a
-// real token, half 1 if it has more than 32), and the half-tiles are
-// scheduled into steps of two slots (X for cube 2j, Y for cube 2j+1):
-//   * a half-tile both cubes selected gets a step of its own, in both slots
-//     (loaded once, used by all four waves);
-//   * the k-th half-tile only cube 2j selected and the k-th only cube 2j+1
-//     selected share a step (X and Y), so neither wave pair idles while the
-//     other works; a side with fewer such half-tiles gets empty slots.
-// Entry layout (uint32): (cube id << 8) | kValid | (half << 5) | (real rows
-// of the half - 1); 0 is an empty slot. Steps are stored as (X, Y) pairs;
-// kStepPad empty steps follow the last one so the fine kernel may read a few
-// steps past the end. Rows with 2 topk > kListSortCap keep the given order
-// and share nothing (all their half-tiles are one-sided).
-constexpr int kListThreads = 256;
-constexpr int kListSortCap = 4096;
-constexpr int kStepPad = 8;
-constexpr uint32_t kValid = 1u << 7;
+// Half-tile list pre-pass: one wave per unit (b, h, query cube). The selected
+// ids (clamped into range: a violated precondition gives unspecified values,
+// never an out-of-bounds access) are sorted ascending and expanded into
+// 32-token half-tiles: half 0 of every cube with a real token, half 1 of
+// every cube with more than 32. Entry = (byte offset of the half from the
+// head's first key row, real rows of the half), two uint32; kListPad (0, 0)
+// entries follow the last one. Rows with topk > kListSortCap keep the given
+// order.
+constexpr int kListSortCap = 1024;
+constexpr int kListPad = 4;
 
-__global__ __launch_bounds__(kListThreads) void steps_kernel(
+__global__ __launch_bounds__(64) void halves_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ vbs,
-    uint32_t* __restrict__ steps, int32_t* __restrict__ counts, int Nq, int Nkv, int topk,
-    int stride, int n_pairs_q) {
+    uint32_t* __restrict__ list, int32_t* __restrict__ counts, int Nkv, int topk, int stride,
+    uint32_t rs2) {
   __shared__ int32_t keys[kListSortCap];
-  __shared__ int32_t part[3][kListThreads / 64];
-  const int pair = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int bh = pair / n_pairs_q, qc0 = 2 * (pair % n_pairs_q);
-  const int32_t* __restrict__ sel = topk_idx + ((size_t)bh * Nq + qc0) * topk;
-  uint32_t* __restrict__ out = steps + (size_t)pair * stride * 2;
-  const int n = (qc0 + 1 < Nq ? 2 : 1) * topk;  // ids of both rows, row 2j first
-  const bool sorted = n <= kListSortCap;
-  // Ids are clamped into range: a violated precondition gives unspecified
-  // values, never an out-of-bounds access. Key = (id << 1) | row.
-  auto key_at = [&](int i) __attribute__((always_inline)) -> int {
-    return (min(max(sel[i], 0), Nkv - 1) << 1) | (i >= topk ? 1 : 0);
+  const int unit = blockIdx.x, lane = threadIdx.x;
+  const int32_t* __restrict__ sel = topk_idx + (size_t)unit * topk;
+  uint32_t* __restrict__ out = list + (size_t)unit * stride * 2;
+  const bool sorted = topk <= kListSortCap;
+  auto id_at = [&](int i) __attribute__((always_inline)) -> int {
+    return min(max(sel[i], 0), Nkv - 1);
   };
   if (sorted) {
     int n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (int i = tid; i < n2; i += kListThreads) keys[i] = i < n ? key_at(i) : 0x7FFFFFFF;
+    while (n2 < topk) n2 <<= 1;
+    for (int i = lane; i < n2; i += 64) keys[i] = i < topk ? id_at(i) : 0x7FFFFFFF;
     for (int size = 2; size <= n2; size <<= 1)
       for (int stride2 = size >> 1; stride2 > 0; stride2 >>= 1) {
         __syncthreads();
-        for (int t = tid; t < (n2 >> 1); t += kListThreads) {
+        for (int t = lane; t < (n2 >> 1); t += 64) {
           const int lo = 2 * t - (t & (stride2 - 1)), hi = lo + stride2;
           const int a = keys[lo], c = keys[hi];
           if (((lo & size) == 0) == (a > c)) {
@@ -276,187 +259,144 @@ __global__ __launch_bounds__(kListThreads) void steps_kernel(
       }
     __syncthreads();
   }
-  // Two passes over the merged list: the first counts the half-tiles of each
-  // class (1: cube 2j only, 2: cube 2j+1 only, 3: both), the second writes
-  // them at their step. In sorted order a cube both rows selected appears as
-  // (id, 0), (id, 1): the first of a run of equal ids carries the run's flags.
-  int total[4] = {0, 0, 0, 0};
-  for (int pass = 0; pass < 2; ++pass) {
-    int base[4] = {0, 0, 0, 0};
-    for (int c0 = 0; c0 < n; c0 += kListThreads) {
-      const int i = c0 + tid;
-      int id = 0, nv = 0, cls = 0;
-      if (i < n) {
-        const int key = sorted ? keys[i] : key_at(i);
-        id = key >> 1;
-        const bool head = !sorted || i == 0 || (keys[i - 1] >> 1) != id;
-        if (head) {
-          cls = 1 << (key & 1);
-          if (sorted && i + 1 < n && (keys[i + 1] >> 1) == id) cls |= 1 << (keys[i + 1] & 1);
-          nv = min(max(vbs[id], 0), kCube);
-        }
-      }
-      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-      int pre = 0;
-#pragma unroll
-      for (int c = 1; c <= 3; ++c) {
-        const uint64_t b1 = __builtin_amdgcn_ballot_w64(cls == c && nv > 0);
-        const uint64_t b2 = __builtin_amdgcn_ballot_w64(cls == c && nv > kHalf);
-        if (cls == c) pre = __builtin_popcountll(b1 & below) + __builtin_popcountll(b2 & below);
-        if (lane == 0) part[c - 1][wave] = __builtin_popcountll(b1) + __builtin_popcountll(b2);
-      }
-      __syncthreads();
-      int off = 0, chunk[4] = {0, 0, 0, 0};
-      for (int w = 0; w < kListThreads / 64; ++w) {
-#pragma unroll
-        for (int c = 1; c <= 3; ++c) {
-          chunk[c] += part[c - 1][w];
-          if (c == cls && w < wave) off += part[c - 1][w];
-        }
-      }
-      if (pass == 1 && nv > 0) {
-        const uint32_t tag = ((uint32_t)id << 8) | kValid;
-        const int r = base[cls] + off + pre;  // rank of half 0 within its class
-        const int s = cls == 3 ? r : total[3] + r;
-        const int slot = cls == 2 ? 1 : 0;
-        const uint32_t e0 = tag | (uint32_t)(min(nv, kHalf) - 1);
-        const uint32_t e1 = tag | (1u << 5) | (uint32_t)(nv - kHalf - 1);
-        if (cls == 3) {
-          out[2 * s] = e0;
-          out[2 * s + 1] = e0;
-          if (nv > kHalf) {
-            out[2 * s + 2] = e1;
-            out[2 * s + 3] = e1;
-          }
-        } else {
-          out[2 * s + slot] = e0;
-          if (nv > kHalf) out[2 * s + 2 + slot] = e1;
-        }
-      }
-#pragma unroll
-      for (int c = 1; c <= 3; ++c) base[c] += chunk[c];
-      __syncthreads();
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;
+  for (int c0 = 0; c0 < topk; c0 += 64) {
+    const int i = c0 + lane;
+    int id = 0, nv = 0;
+    if (i < topk) {
+      id = sorted ? keys[i] : id_at(i);
+      nv = min(max(vbs[id], 0), kCube);
     }
-    if (pass == 0) {
-#pragma unroll
-      for (int c = 1; c <= 3; ++c) total[c] = base[c];
+    const uint64_t b1 = __builtin_amdgcn_ballot_w64(nv > 0);
+    const uint64_t b2 = __builtin_amdgcn_ballot_w64(nv > kHalf);
+    const int pos = base + __builtin_popcountll(b1 & below) + __builtin_popcountll(b2 & below);
+    const uint32_t off0 = (uint32_t)id * (uint32_t)kCube * rs2;
+    if (nv > 0) {
+      out[2 * pos] = off0;
+      out[2 * pos + 1] = (uint32_t)min(nv, kHalf);
     }
+    if (nv > kHalf) {
+      out[2 * pos + 2] = off0 + (uint32_t)kHalf * rs2;
+      out[2 * pos + 3] = (uint32_t)(nv - kHalf);
+    }
+    base += __builtin_popcountll(b1) + __builtin_popcountll(b2);
   }
-  // empty slots on the shorter one-sided list, then the padding steps
-  const int n_one = max(total[1], total[2]);
-  const int n_steps = total[3] + n_one;
-  for (int r = total[1] + tid; r < n_one; r += kListThreads) out[2 * (total[3] + r)] = 0u;
-  for (int r = total[2] + tid; r < n_one; r += kListThreads) out[2 * (total[3] + r) + 1] = 0u;
-  for (int i = tid; i < 2 * kStepPad; i += kListThreads) out[2 * n_steps + i] = 0u;
-  if (tid == 0) counts[pair] = n_steps;
+  if (lane < 2 * kListPad) out[2 * base + lane] = 0u;
+  if (lane == 0) counts[unit] = base;
 }
 
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) void fwd_kernel(
+__global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v16, const uint32_t* __restrict__ steps,
-    const int32_t* __restrict__ counts, uint16_t* __restrict__ out, int Nq, int Nkv,
-    int NH, int step_stride, float scale_log2, int n_pairs, int n_pairs_q) {
+    const uint16_t* __restrict__ v16, const uint32_t* __restrict__ list,
+    const int32_t* __restrict__ counts, uint16_t* __restrict__ out, int Nq, int Nkv, int NH,
+    int list_stride, float scale_log2, int n_units) {
   using S = FwdShape<D>;
-  // [buffer][slot X / Y][half-tile]
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][2][S::kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][S::kHalfBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][S::kHalfBytes];
 
-  const int pair = xcd_remap(blockIdx.x, n_pairs);
-  const int bh = pair / n_pairs_q;
+  const int unit = xcd_remap(blockIdx.x, n_units);
+  const int qc = unit % Nq;
+  const int bh = unit / Nq;
   const int h = bh % NH, b = bh / NH;
   const size_t row_stride = (size_t)NH * D;  // elements between tokens
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int sub = wave >> 1;  // which query cube of the pair this wave serves (slot X / Y)
-  const int qc = 2 * (pair % n_pairs_q) + sub;
-  const bool real_q = qc < Nq;  // false for the second cube of an odd tail
   const int qr = lane & 31, g = lane >> 5;
-  const size_t qrow_idx = (size_t)b * Nq * kCube + (size_t)qc * kCube + 32 * (wave & 1) + qr;
+  const size_t qrow = ((size_t)b * Nq + qc) * kCube + 32 * wave + qr;
 
   // ---- Q of this wave's 32 rows, in the B-operand layout of S^T = K Q^T:
   // lane (column qr, k-group g) holds q[row][16 s + 8 g .. + 7].
   bf16x8 qf[S::kQSteps];
-  uint16_t* const orow = out + qrow_idx * row_stride + (size_t)h * D;
-  if (real_q) {
-    const uint16_t* qrow = q + qrow_idx * row_stride + (size_t)h * D;
+  {
+    const uint16_t* q0 = q + qrow * row_stride + (size_t)h * D;
 #pragma unroll
-    for (int s = 0; s < S::kQSteps; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * g);
-  } else {
-#pragma unroll
-    for (int s = 0; s < S::kQSteps; ++s) qf[s] = bf16x8{};
+    for (int s = 0; s < S::kQSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(q0 + 16 * s + 8 * g);
   }
+  uint16_t* const orow = out + qrow * row_stride + (size_t)h * D;
 
-  // ---- the pair's step list (built by the pre-pass): step i holds the
-  // entries of slots X and Y. Reads stay below n_steps + 3, inside the padded
-  // list. Scalar loads: the index is made wave-uniform explicitly, since a
-  // vector load here would be counted by the explicit vmcnt waits.
-  const uint32_t* __restrict__ lst = steps + (size_t)pair * step_stride * 2;
-  const int n_steps = __builtin_amdgcn_readfirstlane(counts[pair]);
-  auto ent = [&](int i, int slot) __attribute__((always_inline)) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)lst[2 * __builtin_amdgcn_readfirstlane(i) + slot]);
+  // ---- the unit's half-tiles; reads past the list (i >= n) see the (0, 0)
+  // padding entries (i < n + kListPad)
+  const uint32_t* __restrict__ lst = list + (size_t)unit * list_stride * 2;
+  const int n = __builtin_amdgcn_readfirstlane(counts[unit]);
+  auto ent = [&](int i) __attribute__((always_inline)) -> u32x2 {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(lst + 2 * __builtin_amdgcn_readfirstlane(i));
+    return u32x2{(uint32_t)__builtin_amdgcn_readfirstlane((int)v[0]),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)v[1])};
   };
-  if (n_steps == 0) {  // no real key in any cube either row selected: the rows are 0
-    if (real_q) {
+  if (n == 0) {  // no real key in any selected cube: the rows are 0
 #pragma unroll
-      for (int db = 0; db < S::kDBlocks; ++db)
+    for (int db = 0; db < S::kDBlocks; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * g) = u32x2{0u, 0u};
-    }
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * g) = u32x2{0u, 0u};
     return;
   }
 
-  // ---- DMA: each wave-wide load fills 1 KiB of a half-tile buffer, lane L
-  // writing bytes [16 L, 16 L + 16); the lane fetches the global chunk that
-  // the swizzle places in that slot. Wave w loads rows [8 w, 8 w + 8) of
-  // both slots' half-tiles. The buffer range ends at the half's real rows,
-  // so padding rows land in LDS as zeros; an empty slot, or slot Y of a
-  // shared step, gets an empty range (its loads move no data and only write
-  // zeros), which keeps the wait counts constant. Byte offsets are
-  // < 32 * NH * D * 2 < 2^31 (host-checked).
+  // ---- loads: wave w fills KiB [L w, L w + L) of every half-tile buffer
+  // (L = kLoads), lane L' writing bytes [16 L', 16 L' + 16) of a KiB; the
+  // lane fetches the global chunk that the swizzle places in that slot.
+  // Byte offsets stay below 2^32 (host-checked).
+  constexpr int L = S::kLoads;
   const uint32_t rs2 = (uint32_t)NH * D * 2u;
-  uint32_t koff[S::kLoads], voff[S::kLoads];
+  uint32_t koff[L], voff[L];
 #pragma unroll
-  for (int n = 0; n < S::kLoads; ++n) {
-    const int row = (wave * S::kLoads + n) * S::kRowsPerKiB + lane / S::kChunks;
+  for (int m = 0; m < L; ++m) {
+    const int row = (wave * L + m) * S::kRowsPerKiB + lane / S::kChunks;
     const int slot = lane % S::kChunks;
-    koff[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_k<D>(row));
-    voff[n] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_v<D>(row));
+    koff[m] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_k<D>(row)) - 1024u * (m & 1);
+    voff[m] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_v<D>(row)) - 1024u * (m & 1);
   }
-  const uint32_t lds_wave = (uint32_t)(wave * S::kLoads) * 1024u;
+  const uint32_t lds_wave = (uint32_t)(wave * L) * 1024u;
   const size_t kv_head = (size_t)b * Nkv * kCube * row_stride + (size_t)h * D;
-  auto half_rsrc = [&](const uint16_t* base, uint32_t e, bool real) __attribute__((always_inline)) -> int32x4_t {
-    const uint16_t* p =
-        base + kv_head + ((size_t)(e >> 8) * kCube + kHalf * ((e >> 5) & 1)) * row_stride;
-    return buffer_rsrc(p, real ? (int)((((e & 31) + 1) * rs2)) : 0);
+  const uint64_t kbase = reinterpret_cast<uint64_t>(k + kv_head);
+  const uint64_t vbase = reinterpret_cast<uint64_t>(v16 + kv_head);
+  // gfx9 raw buffer descriptor of one half-tile: base + offset, range = its
+  // real rows (the loads of padding rows and of (0, 0) entries return zeros)
+  auto mk_rsrc = [&](uint64_t base, const u32x2& e) __attribute__((always_inline)) -> int32x4_t {
+    const uint64_t a = base + e[0];
+    int32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)(e[1] * rs2));
+    r[3] = kBufferDword3;
+    return r;
   };
-  // resources of both slots of a step: X loads unless empty, Y loads unless
-  // empty or equal to X
-  struct Pair2 {
-    int32x4_t x, y;
+  const uint32_t kb0 = lds_address(kbuf), vb0 = lds_address(vbuf);
+  // load pair p (0 <= p < L / 2) of a half-tile into buffer `buf`
+  auto dma_k = [&](const int32x4_t& r, int buf, int p) __attribute__((always_inline)) {
+    dma16x2(r, koff[2 * p], koff[2 * p + 1], kb0 + (uint32_t)buf * S::kHalfBytes + lds_wave + 2048u * p);
   };
-  auto step_rsrc = [&](const uint16_t* base, uint32_t ex, uint32_t ey) __attribute__((always_inline)) -> Pair2 {
-    return Pair2{half_rsrc(base, ex, (ex & kValid) != 0),
-                 half_rsrc(base, ey, (ey & kValid) != 0 && ey != ex)};
+  auto dma_v = [&](const int32x4_t& r, int buf, int p) __attribute__((always_inline)) {
+    dma16x2(r, voff[2 * p], voff[2 * p + 1], vb0 + (uint32_t)buf * S::kHalfBytes + lds_wave + 2048u * p);
   };
-  // DMA j (0 <= j < 2 kLoads) of a step's tensor: the first kLoads fill slot
-  // X, the rest slot Y
-  auto dma_j = [&](const Pair2& r, uint32_t lds_buf, const uint32_t* off, int j) __attribute__((always_inline)) {
-    if (j < S::kLoads)
-      dma16(r.x, off[j], lds_buf + lds_wave + 1024u * j);
-    else
-      dma16(r.y, off[j - S::kLoads], lds_buf + (uint32_t)S::kHalfBytes + lds_wave + 1024u * (j - S::kLoads));
-  };
-  auto issue_all = [&](const Pair2& r, uint32_t lds_buf, const uint32_t* off) __attribute__((always_inline)) {
+
+  // ---- per-lane LDS read addresses in buffer 0 (buffer 1 is a constant
+  // offset away). K: chunk 2 st + g of row qr. V^T: rows 16 kk + trow (+8),
+  // columns 32 db + dcol; since the V swizzle depends on the row mod 4 only,
+  // kk and the +8 rows are constant offsets too. The transposing read: in each
+  // 16-lane group, lane i receives element i%4 of the 8 bytes that lane
+  // 4e + i/4 addressed, for e = 0..3. Lane (group G, s) addresses row
+  // base + 4(G/2) + s/4 at column block 32 db + 16 (G%2) + 4 (s%4), so lane l
+  // receives d = 32 db + l%32 at tokens base + 4 (l/32) + e: the k-slots of
+  // lane group g = l/32 are tokens base+4g+{0..3} and base+8+4g+{0..3},
+  // matching the accumulator layout of P.
+  const uint8_t* kl[S::kQSteps];
 #pragma unroll
-    for (int j = 0; j < 2 * S::kLoads; ++j) dma_j(r, lds_buf, off, j);
-  };
+  for (int st = 0; st < S::kQSteps; ++st)
+    kl[st] = &kbuf[0][0] + qr * S::kRowBytes + 16 * ((2 * st + g) ^ swz_k<D>(qr));
+  const int Gq = lane >> 4, s4 = lane & 15;
+  const int trow = 4 * (Gq >> 1) + (s4 >> 2);
+  const int dcol = 16 * (Gq & 1) + 4 * (s4 & 3);
+  const uint8_t* vl[S::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < S::kDBlocks; ++db) {
+    const int d0 = 32 * db + dcol;
+    vl[db] = &vbuf[0][0] + trow * S::kRowBytes + 16 * ((d0 >> 3) ^ swz_v<D>(trow)) + 2 * (d0 & 7);
+  }
 
   floatx16 oacc[S::kDBlocks];
 #pragma unroll
@@ -464,203 +404,175 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
   // m_ref: reference max (raw score units) the probabilities are taken
-  // against; l_run: running sum of exp2((s - m_ref) * scale_log2).
-  float m_ref = kNegInf, l_run = 0.0f;
+  // against; l_run: running sum of exp2((s - m_ref) * scale_log2); alpha and
+  // need_rescale: the pending O rescale after a raise of m_ref
+  float m_ref = kNegInf, l_run = 0.0f, alpha = 1.0f;
+  bool need_rescale = false;
   const floatx16 zero16 = {};
   const halfx2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // The Q loads must be complete before the first DMA is issued: afterwards
-  // the only outstanding vector-memory operations are the tile loads that
-  // the explicit waits account for. The empty asm makes the compiler place
-  // its own wait for Q here rather than inside the loop.
+  // S^T = K Q^T for the half-tile in K buffer kbi; V load pairs ride along
+  auto qk = [&](int kbi, floatx16& s, const int32x4_t& vr, int vbi) __attribute__((always_inline)) {
 #pragma unroll
-  for (int s = 0; s < S::kQSteps; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[s])));
-
-  // ---- pipeline over steps. Buffers alternate: step i uses kbuf[i&1] and
-  // vbuf[i&1]. V(i+1) streams in during QK(i) (its buffer held V(i-1), which
-  // every wave finished before the first barrier of step i); K(i+2) streams
-  // in during PV(i) (its buffer held K(i), which every wave finished before
-  // the second barrier of step i). Each step's DMAs are spread one per MFMA
-  // step; a wave whose slot is empty in step i issues them back to back and
-  // skips the arithmetic. The prologue loads K(0), V(0) and K(1). Loads of
-  // steps past the end of the list are issued with empty slots, so every
-  // wait below leaves exactly the two younger steps' loads in flight.
-  constexpr int kPerStep = 2 * S::kLoads;  // DMAs per wave, tensor and step
-  const uint32_t kb0 = lds_address(kbuf), vb0 = lds_address(vbuf);
-  constexpr uint32_t kBufBytes = 2u * S::kHalfBytes;
-  uint32_t x_c = ent(0, 0), y_c = ent(0, 1), x_n1 = ent(1, 0), y_n1 = ent(1, 1);
-  issue_all(step_rsrc(k, x_c, y_c), kb0, koff);
-  issue_all(step_rsrc(k, x_n1, y_n1), kb0 + kBufBytes, koff);
-
-  const int G = lane >> 4, s4 = lane & 15;
-  const int trow = 4 * (G >> 1) + (s4 >> 2);
-  const int dcol = 16 * (G & 1) + 4 * (s4 & 3);
-  // this wave's entry of a step, and the slot its tiles sit in (slot X for a
-  // shared step)
-  auto my_entry = [&](uint32_t ex, uint32_t ey) __attribute__((always_inline)) -> uint32_t {
-    return sub == 0 ? ex : ey;
-  };
-  auto my_slot = [&](uint32_t ex, uint32_t ey) __attribute__((always_inline)) -> uint32_t {
-    return (sub == 0 || ex == ey) ? 0u : (uint32_t)S::kHalfBytes;
-  };
-  // Steps in which this wave's slot is empty run in the inner loop, which
-  // only keeps the loads going; the accumulators are carried by the outer
-  // loop alone.
-  int i = 0;
-#pragma unroll 1
-  while (true) {
-#pragma unroll 1
-    while (i < n_steps && (my_entry(x_c, y_c) & kValid) == 0) {
-      const uint32_t x_n2 = ent(i + 2, 0), y_n2 = ent(i + 2, 1);
-      wait_vmcnt<kPerStep>();
-      __syncthreads();
-      issue_all(step_rsrc(v16, x_c, y_c), vb0, voff);
-      wait_vmcnt<0>();
-      __syncthreads();
-      issue_all(step_rsrc(k, x_n2, y_n2), kb0 + kBufBytes * (uint32_t)(i & 1), koff);
-      x_c = x_n1;
-      y_c = y_n1;
-      x_n1 = x_n2;
-      y_n1 = y_n2;
-      ++i;
+    for (int st = 0; st < S::kQSteps; ++st) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl[st] + kbi * S::kHalfBytes);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? zero16 : s, 0, 0, 0);
+      if (vbi >= 0 && st % 2 == 1 && st / 2 < L / 2) dma_v(vr, vbi, st / 2);
     }
-    if (i >= n_steps) break;
-    const uint32_t x_n2 = ent(i + 2, 0), y_n2 = ent(i + 2, 1);
-    const uint32_t e_c = my_entry(x_c, y_c);
-    const uint32_t sl = my_slot(x_c, y_c);
-
-    // ---- K(i) has landed (K(i+1) may be in flight), then every wave's
-    // loads are visible; every wave has finished PV(i-1), so the V buffer is
-    // free for V(i)
-    wait_vmcnt<kPerStep>();
-    __syncthreads();
-
-    // ---- S^T = K Q^T over the half's 32 tokens; the K operands are read
-    // from LDS two k-steps ahead of the MFMAs that consume them. V(i+1)'s
-    // DMAs ride along.
-    floatx16 sacc;
-    {
-      const Pair2 vr = step_rsrc(v16, x_c, y_c);
-      const uint32_t vlds = vb0;
-      const uint8_t* krow = &kbuf[i & 1][0][0] + sl + qr * S::kRowBytes;
-      const int ksw = swz_k<D>(qr);
-      bf16x8 a[3];
-      auto rd = [&](int st) __attribute__((always_inline)) {
-        a[st % 3] = *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * st + g) ^ ksw));
-      };
-      rd(0);
-      rd(1);
+  };
+  // O^T += V^T P^T for the half-tile in V buffer vbi; K load pairs ride along
+  auto pv = [&](int vbi, const halfx8 (&pb)[2], const int32x4_t& kr, int kbi) __attribute__((always_inline)) {
+    constexpr int NSTEP = 2 * S::kDBlocks;  // (kk, db)
 #pragma unroll
-      for (int st = 0; st < S::kQSteps; ++st) {
-        if (st + 2 < S::kQSteps) rd(st + 2);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[st % 3], qf[st], st == 0 ? zero16 : sacc,
-                                                       0, 0, 0);
-        if (st < kPerStep) dma_j(vr, vlds, voff, st);
-      }
-#pragma unroll
-      for (int j = S::kQSteps; j < kPerStep; ++j) dma_j(vr, vlds, voff, j);
+    for (int st = 0; st < NSTEP; ++st) {
+      const int kk = st / S::kDBlocks, db = st % S::kDBlocks;
+      const uint8_t* p0 = vl[db] + vbi * S::kHalfBytes + kk * 16 * S::kRowBytes;
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p0)));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p0 + 8 * S::kRowBytes)));
+      const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a), pb[kk], oacc[db], 0, 0, 0);
+      if (kbi >= 0 && st % 2 == 1 && st / 2 < L / 2) dma_k(kr, kbi, st / 2);
     }
-
-    // ---- online softmax of the half: tokens >= its real rows set to -inf
-    // (partial halves only; the asm keeps the compiler from flattening the
-    // branch into selects that every half would execute), row max, lazy
-    // raise of the reference max (wave-uniform), P in fp16 (round to nearest
-    // even), row sum of the same rounded values (v_dot2_f32_f16 against 1.0).
-    {
-      const int nvh = (int)(e_c & 31u) + 1;
-      if (nvh < kHalf) {
-        asm volatile("");
+  };
+  // tokens >= the half's real rows set to -inf (partial halves only; the asm
+  // keeps the compiler from flattening the branch into selects that every
+  // half would execute), row max, lazy raise of the reference max
+  // (wave-uniform decision)
+  auto mask_max = [&](uint32_t nvh, floatx16& s) __attribute__((always_inline)) {
+    if (nvh < (uint32_t)kHalf) {
+      asm volatile("");
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = 8 * (r >> 2) + 4 * g + (r & 3);
-          if (tok >= nvh) sacc[r] = kNegInf;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t tok = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (tok >= nvh) s[r] = kNegInf;
       }
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = halves_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx * scale_log2 > m_ref * scale_log2 + kRescaleThreshold) != 0) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = m_ref == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
+    const bool up = mx * scale_log2 > m_ref * scale_log2 + kRescaleThreshold;
+    need_rescale = __builtin_amdgcn_ballot_w64(up) != 0;
+    if (need_rescale) {
+      const float m_new = up ? mx : m_ref;
+      alpha = m_ref == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
       m_ref = m_new;
       l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < S::kDBlocks; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    const float mc = m_ref == kNegInf ? 0.0f : m_ref * scale_log2;
-    halfx8 pb[2];
-    float rs_sum = 0.0f;
+  };
+  // P in fp16 (round to nearest even) and the row sums of the same rounded
+  // values (v_dot2_f32_f16 against 1.0). Every row has a finite m_ref here:
+  // the first half-tile of a unit holds at least one real token.
+  auto exp_sum = [&](const floatx16& s, halfx8 (&pb)[2]) __attribute__((always_inline)) {
+    const float mc = m_ref * scale_log2;
+    float rs = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       floatx8 p;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 * kk + e], scale_log2, -mc));
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kk + e], scale_log2, -mc));
       pb[kk] = __builtin_convertvector(p, halfx8);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const halfx2 two = {pb[kk][e], pb[kk][e + 1]};
-        rs_sum = __builtin_amdgcn_fdot2(two, ones, rs_sum, false);
+        rs = __builtin_amdgcn_fdot2(two, ones, rs, false);
       }
     }
-    l_run += halves_sum(rs_sum);
+    l_run += halves_sum(rs);
+  };
+  auto rescale = [&]() __attribute__((always_inline)) {
+    if (need_rescale) {
+#pragma unroll
+      for (int db = 0; db < S::kDBlocks; ++db) oacc[db] *= alpha;
+    }
+  };
 
-    // ---- V(i) (and K(i+1)) have landed, then every wave's loads are
-    // visible; every wave has finished QK(i), so K(i)'s buffer is free for
-    // K(i+2).
-    wait_vmcnt<0>();
+  // The Q loads must be complete before the first tile load is issued:
+  // afterwards the only outstanding vector-memory operations are the tile
+  // loads that the explicit waits account for. The empty asm makes the
+  // compiler place its own wait for Q here rather than inside the loop.
+#pragma unroll
+  for (int s = 0; s < S::kQSteps; ++s) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qf[s])));
+
+  // ---- prologue: K(0), K(1), V(0) in flight; QK(0) and its max
+  floatx16 sA, sB;
+  halfx8 pb[2];
+  u32x2 e_n1 = ent(1), e_n2 = ent(2);
+  {
+    const u32x2 e0 = ent(0);
+    const int32x4_t r0 = mk_rsrc(kbase, e0), r1 = mk_rsrc(kbase, e_n1), r2 = mk_rsrc(vbase, e0);
+#pragma unroll
+    for (int p = 0; p < L / 2; ++p) dma_k(r0, 0, p);
+#pragma unroll
+    for (int p = 0; p < L / 2; ++p) dma_k(r1, 1, p);
+#pragma unroll
+    for (int p = 0; p < L / 2; ++p) dma_v(r2, 0, p);
+    wait_vmcnt<2 * L>();  // K(0): K(1), V(0) may be in flight
     __syncthreads();
-
-    // ---- O^T += V^T P^T. The A operand comes from the transposing read: in
-    // each 16-lane group, lane i receives element i%4 of the 8 bytes that
-    // lane 4e + i/4 addressed, for e = 0..3. Lane (group G, s) addresses row
-    // base + 4(G/2) + s/4 at column block 32 db + 16 (G%2) + 4 (s%4), so lane
-    // l receives d = 32 db + l%32 at tokens base + 4 (l/32) + e: the k-slots
-    // of lane group g = l/32 are tokens base+4g+{0..3} and base+8+4g+{0..3},
-    // matching the accumulator layout of P. Operands are read two MFMAs
-    // ahead. K(i+2)'s DMAs ride along.
-    {
-      const Pair2 kr = step_rsrc(k, x_n2, y_n2);
-      const uint32_t klds = kb0 + kBufBytes * (uint32_t)(i & 1);
-      const uint8_t* vb = &vbuf[0][0] + sl;
-      constexpr int NSTEP = 2 * S::kDBlocks;  // (kk, db)
-      u32x4 a[3];
-      auto rd = [&](int st) __attribute__((always_inline)) {
-        const int kk = st / S::kDBlocks, db = st % S::kDBlocks;
-        const int r0 = 16 * kk + trow, r1 = r0 + 8;
-        const int d0 = 32 * db + dcol;
-        const uint8_t* p0 = vb + r0 * S::kRowBytes + 16 * ((d0 >> 3) ^ swz_v<D>(r0)) + 2 * (d0 & 7);
-        const uint8_t* p1 = vb + r1 * S::kRowBytes + 16 * ((d0 >> 3) ^ swz_v<D>(r1)) + 2 * (d0 & 7);
-        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p0)));
-        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p1)));
-        a[st % 3] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      };
-      rd(0);
-      rd(1);
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        if (st + 2 < NSTEP) rd(st + 2);
-        const int kk = st / S::kDBlocks, db = st % S::kDBlocks;
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a[st % 3]),
-                                                          pb[kk], oacc[db], 0, 0, 0);
-        if (st < kPerStep) dma_j(kr, klds, koff, st);
-      }
-#pragma unroll
-      for (int j = NSTEP; j < kPerStep; ++j) dma_j(kr, klds, koff, j);
-    }
-    x_c = x_n1;
-    y_c = y_n1;
-    x_n1 = x_n2;
-    y_n1 = y_n2;
-    ++i;
+    qk(0, sA, r0, -1);
+    mask_max(e0[1], sA);
+    need_rescale = false;  // O and l are still zero
   }
 
-  wait_vmcnt<0>();  // the empty loads of the last steps
-  if (!real_q) return;
+  // Step j (0 <= j < n - 1), parity P = j & 1: S(j) in sc, S(j+1) into sn.
+  //   A(j): K(j+1) landed; O rescale; QK(j+1) with V(j+1)'s loads; P(j)
+  //   B(j): V(j) landed; PV(j) with K(j+3)'s loads; mask and max of S(j+1)
+  // K(i) and V(i) sit in buffer i & 1. K(j+3) reuses the buffer of K(j+1),
+  // which every wave finished in A(j) (the barrier of B(j) certifies it);
+  // V(j+1) reuses that of V(j-1), finished in B(j-1) (the barrier of A(j)).
+  // Issue order: K0 K1 V0 | A(0): K2 V1 | B(0): K3 | A(1): V2 | B(1): K4 ...;
+  // from A(1) on every wait leaves the two most recent tiles in flight.
+  auto step = [&](auto Pc, int j) __attribute__((always_inline)) {
+    constexpr int P = decltype(Pc)::value;
+    floatx16& sc = P ? sB : sA;
+    floatx16& sn = P ? sA : sB;
+    const u32x2 e_n3 = ent(j + 3);
+    if (j == 0) {
+      wait_vmcnt<L>();  // K(1): V(0) may be in flight
+      __syncthreads();
+      const int32x4_t r2 = mk_rsrc(kbase, e_n2);
+#pragma unroll
+      for (int p = 0; p < L / 2; ++p) dma_k(r2, 0, p);
+    } else {
+      wait_vmcnt<2 * L>();  // K(j+1)
+      __syncthreads();
+    }
+    rescale();
+    qk(P ^ 1, sn, mk_rsrc(vbase, e_n1), P ^ 1);
+    exp_sum(sc, pb);
+    wait_vmcnt<2 * L>();  // V(j)
+    __syncthreads();
+    pv(P, pb, mk_rsrc(kbase, e_n3), P ^ 1);
+    mask_max(e_n1[1], sn);
+    e_n1 = e_n2;
+    e_n2 = e_n3;
+  };
+  int j = 0;
+  if (n > 1) {
+    step(IC<0>{}, 0);
+    j = 1;
+#pragma unroll 1
+    while (j + 1 < n) {
+      step(IC<1>{}, j);
+      ++j;
+      if (j + 1 >= n) break;
+      step(IC<0>{}, j);
+      ++j;
+    }
+  }
+  // ---- the last step: P(n-1) and PV(n-1); V(n-1) sits in vbuf[(n-1) & 1]
+  {
+    rescale();
+    exp_sum((j & 1) ? sB : sA, pb);
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int32x4_t none = mk_rsrc(kbase, u32x2{0u, 0u});
+    if (j & 1)
+      pv(1, pb, none, -1);
+    else
+      pv(0, pb, none, -1);
+  }
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32 db + 8 (r/4) + 4 g + r%4
   const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
@@ -679,12 +591,12 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk) {
   auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
   FwdWorkspace w;
-  w.list_stride = 2 * topk + kStepPad;  // steps per pair, 8 bytes each
-  const size_t pairs = (size_t)B * NH * ((Nq + 1) / 2);
+  w.list_stride = 2 * topk + kListPad;  // entries per unit, 8 bytes each
+  const size_t units = (size_t)B * NH * Nq;
   w.v16_off = 0;
   w.list_off = up((size_t)B * Nkv * kCube * NH * D * 2);
-  w.count_off = w.list_off + up(pairs * w.list_stride * 8);
-  w.total = w.count_off + up(pairs * 4);
+  w.count_off = w.list_off + up(units * w.list_stride * 8);
+  w.total = w.count_off + up(units * 4);
   return w;
 }
 
@@ -695,29 +607,28 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   const FwdWorkspace w = fwd_workspace(B, Nq, Nkv, NH, D, topk);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(ws + w.v16_off);
-  uint32_t* steps = reinterpret_cast<uint32_t*>(ws + w.list_off);
+  uint32_t* list = reinterpret_cast<uint32_t*>(ws + w.list_off);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.count_off);
   const int cpr = NH * D / 8;
-  const int n_pairs_q = (Nq + 1) / 2;
-  const int n_pairs = B * NH * n_pairs_q;
+  const int n_units = B * NH * Nq;
   hipLaunchKernelGGL(v_to_fp16_kernel, dim3(Nkv * kCvtSplit, B), dim3(kCvtThreads), 0, stream,
                      reinterpret_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(v16), vbs, Nkv,
                      cpr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(steps_kernel, dim3(n_pairs), dim3(kListThreads), 0, stream, topk_idx, vbs,
-                     steps, counts, Nq, Nkv, topk, w.list_stride, n_pairs_q);
+  hipLaunchKernelGGL(halves_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, vbs, list,
+                     counts, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   if (D == 128)
-    hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_pairs), dim3(FwdShape<128>::kThreads), 0,
-                       stream, q, k, v16, steps, counts, out, Nq, Nkv, NH, w.list_stride,
-                       scale_log2, n_pairs, n_pairs_q);
+    hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_units), dim3(FwdShape<128>::kThreads), 0, stream,
+                       q, k, v16, list, counts, out, Nq, Nkv, NH, w.list_stride, scale_log2,
+                       n_units);
   else
-    hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_pairs), dim3(FwdShape<64>::kThreads), 0,
-                       stream, q, k, v16, steps, counts, out, Nq, Nkv, NH, w.list_stride,
-                       scale_log2, n_pairs, n_pairs_q);
+    hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_units), dim3(FwdShape<64>::kThreads), 0, stream,
+                       q, k, v16, list, counts, out, Nq, Nkv, NH, w.list_stride, scale_log2,
+                       n_units);
   return hipGetLastError();
 }
 
