@@ -177,6 +177,39 @@ int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
                 int32_t topk, float sm_scale, void* workspace,
                 size_t workspace_bytes, vsa_stream_t stream);
 
+/* Fine stage driven by a lookup table with a per-row block count, plus
+ * optional per-row softmax statistics. VSA blog, "Block-Sparse Encoding"
+ * (kv_block_idx with valid_block_num, the number of valid blocks per query
+ * row) and "Sparse Traversal" (the kernel visits the first valid_block_num
+ * entries of its row); Wan INT8 blog, "Dynamic Sparsity Budgeting via Softmax
+ * Normalizer Registers" (max_prob = 1 / l, l = sum_j exp(s_j - max_j s_j)).
+ * Computes what vsa_fwd computes for a row of the first
+ * valid_block_num[b][h][c] ids of kv_block_idx[b][h][c][0 .. max_kv); the
+ * other entries of the row are not read.
+ *   kv_block_idx    [B][NH][Nq][max_kv] int32; the used entries are distinct
+ *                   ids in [0, Nkv) (a precondition, as for vsa_fwd)
+ *   valid_block_num [B][NH][Nq] int32 device array, each in [0, max_kv]
+ *                   (values outside are clamped); NULL means max_kv for every
+ *                   row. A count of 0 gives zero output rows.
+ *   lse             [B][NH][Nq*64] float32 device array or NULL: per query row,
+ *                   the natural-log log-sum-exp of its scaled scores over the
+ *                   real keys it attends, log sum_j exp(sm_scale q.k_j); -inf
+ *                   for a row without keys
+ *   max_prob        [B][NH][Nq*64] float32 device array or NULL: per query
+ *                   row, its largest softmax weight 1 / sum_j exp(sm_scale
+ *                   (q.k_j - max_i q.k_i)); 0 for a row without keys
+ * The workspace is vsa_fwd_workspace_bytes(B, Nq, Nkv, NH, D, max_kv) bytes.
+ * lse and max_prob must be 4-byte aligned; every other argument is as for
+ * vsa_fwd. The statistics come from the same fp32 running max and the sum of
+ * the same fp16-rounded weights that normalise the output. Errors: as for
+ * vsa_fwd. */
+int32_t vsa_fwd_lut(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                    const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                    const int32_t* vbs, vsa_bf16_t* out, float* lse, float* max_prob,
+                    int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                    int32_t max_kv, float sm_scale, void* workspace,
+                    size_t workspace_bytes, vsa_stream_t stream);
+
 /* Checks the vsa_fwd precondition on topk_idx on the device: counts, into
  * *bad_count (one int32 in device memory, which the caller zeroes first), the
  * entries that are outside [0, Nkv) or repeat an earlier id of their row

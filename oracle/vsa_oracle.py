@@ -31,6 +31,13 @@ What it computes, and where the pages define it:
   the selected key/value cubes.
   Pages: dataset card, "Operator contract"; VSA blog, "Two-Stage Architecture"
   Stage 2 and "Sparse Traversal".
+* ``fwd_lut`` -- the same over the first valid_block_num[b, h, c] entries of
+  each index row, with two per-row statistics: the log-sum-exp of the scaled
+  scores and max_prob = 1 / l, l = sum_j exp(s_j - max_i s_i).
+  Pages: VSA blog, "Block-Sparse Encoding" (kv_block_idx + valid_block_num)
+  and "Sparse Traversal" (the kernel loops over valid_block_num[query_block]
+  entries); Wan INT8 blog, "Dynamic Sparsity Budgeting via Softmax
+  Normalizer Registers" (max_prob = 1 / l_i).
 
 Readings where the pages are silent (each one is listed with its reason in
 the design notes of the repository):
@@ -46,7 +53,9 @@ the design notes of the repository):
 7. Padding query rows are computed exactly like real rows.
 8. sm_scale defaults to 1/sqrt(D).
 9. ``topk_idx`` rows hold distinct ids in [0, Nkv) (asserted).
-10. A row whose selected cubes hold no real token outputs 0.
+10. A row whose selected cubes hold no real token outputs 0 (and, in
+    ``fwd_lut``, lse = -inf and max_prob = 0).
+11. The log-sum-exp is natural-log, over the scaled scores sm_scale q.k_j.
 """
 from __future__ import annotations
 
@@ -70,6 +79,8 @@ __all__ = [
     "fwd_unit",
     "fwd",
     "fwd_units",
+    "fwd_unit_stats",
+    "fwd_lut",
 ]
 
 #: tokens per cube edge (the VSA blog: (Ct, Ch, Cw) = (4, 4, 4))
@@ -316,3 +327,53 @@ def fwd(q_t, k_t, v_t, topk_idx, vbs, sm_scale=None) -> np.ndarray:
                 out[b, c * CUBE:(c + 1) * CUBE, h, :] = fwd_unit(
                     q_t, k_t, v_t, topk_idx, vbs, b, h, c, sm_scale)
     return out
+
+
+def fwd_unit_stats(q_t, k_t, v_t, ids, vbs, b: int, h: int, c: int,
+                   sm_scale: float | None = None):
+    """Rows of query cube c of (b, h) attending the real tokens of cubes ``ids``:
+    (out (64, D), lse (64,), max_prob (64,)), float64.
+
+    VSA blog, "Sparse Traversal": only the listed blocks are visited. Wan INT8
+    blog, "Dynamic Sparsity Budgeting via Softmax Normalizer Registers": with
+    m_i the row max and l_i = sum_j exp(s_ij - m_i), max_prob_i = 1 / l_i;
+    the log-sum-exp of the row is m_i + log l_i.
+    """
+    D = q_t.shape[-1]
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    rows = _selected_rows(np.asarray(ids), np.asarray(vbs))
+    if rows.size == 0:
+        return (np.zeros((CUBE, D)), np.full(CUBE, -np.inf), np.zeros(CUBE))
+    q = np.asarray(q_t[b, c * CUBE:(c + 1) * CUBE, h, :], dtype=np.float64)
+    K = np.asarray(k_t[b, rows, h, :], dtype=np.float64)
+    V = np.asarray(v_t[b, rows, h, :], dtype=np.float64)
+    s = (q @ K.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1)
+    return (p @ V) / l[:, None], m[:, 0] + np.log(l), 1.0 / l
+
+
+def fwd_lut(q_t, k_t, v_t, kv_block_idx, valid_block_num, vbs, sm_scale=None):
+    """Fine stage driven by a block lookup table: query cube (b, h, c) attends
+    the first valid_block_num[b, h, c] ids of kv_block_idx[b, h, c]
+    (all of them if valid_block_num is None). Returns out (B, Nq*64, NH, D),
+    lse and max_prob (B, NH, Nq*64), float64."""
+    B, S, NH, D = q_t.shape
+    Nq = S // CUBE
+    assert kv_block_idx.shape[:3] == (B, NH, Nq), kv_block_idx.shape
+    max_kv = kv_block_idx.shape[3]
+    out = np.empty((B, S, NH, D))
+    lse = np.empty((B, NH, S))
+    mp = np.empty((B, NH, S))
+    for b in range(B):
+        for h in range(NH):
+            for c in range(Nq):
+                n = max_kv if valid_block_num is None else int(valid_block_num[b, h, c])
+                assert 0 <= n <= max_kv, "valid_block_num outside [0, max_kv]"
+                o, e, x = fwd_unit_stats(q_t, k_t, v_t, kv_block_idx[b, h, c, :n], vbs, b, h, c,
+                                         sm_scale)
+                out[b, c * CUBE:(c + 1) * CUBE, h, :] = o
+                lse[b, h, c * CUBE:(c + 1) * CUBE] = e
+                mp[b, h, c * CUBE:(c + 1) * CUBE] = x
+    return out, lse, mp

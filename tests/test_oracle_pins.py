@@ -370,3 +370,87 @@ def test_fwd_rejects_bad_indices():
     idx[..., 1] = 8                                     # out of range
     with pytest.raises(AssertionError):
         oracle.fwd(q, k, v, idx, vbs)
+
+
+# ---------------------------------------------- lookup table and row statistics
+
+def test_fwd_lut_full_counts_equals_fwd():
+    q, kk, v, vbs = _tiled_case(5, 6, 7, NH=2, D=16, B=2)
+    idx = _random_topk(2, 2, vbs.size, 4)
+    out, _, _ = oracle.fwd_lut(q, kk, v, idx, None, vbs)
+    np.testing.assert_array_equal(out, oracle.fwd(q, kk, v, idx, vbs))
+    full = np.full(idx.shape[:3], 4, np.int32)
+    out2, _, _ = oracle.fwd_lut(q, kk, v, idx, full, vbs)
+    np.testing.assert_array_equal(out2, out)
+
+
+def test_fwd_lut_counts_equal_truncated_rows_and_dense_mask():
+    """valid_block_num = n uses exactly the first n ids of each row: equal to
+    the brute-force masked attention over those ids (rows with n = 0 are 0)."""
+    rng = np.random.default_rng(7)
+    q, kk, v, vbs = _tiled_case(9, 5, 6, NH=2, D=8, B=1, rng=rng)
+    Nc = vbs.size
+    idx = _random_topk(1, 2, Nc, 5, rng=rng)
+    valid = rng.integers(1, 6, size=(1, 2, Nc)).astype(np.int32)
+    valid[0, 0, 0] = 0
+    out, lse, mp = oracle.fwd_lut(q, kk, v, idx, valid, vbs)
+    scale = 1 / math.sqrt(8)
+    for h in range(2):
+        for c in range(Nc):
+            n = int(valid[0, h, c])
+            rows = slice(64 * c, 64 * (c + 1))
+            if n == 0:
+                assert np.all(out[0, rows, h] == 0) and np.all(np.isneginf(lse[0, h, rows]))
+                assert np.all(mp[0, h, rows] == 0)
+                continue
+            # a row-specific dense reference: only row (h, c) matters here
+            sub_full = np.repeat(idx[:, :, :, :1], n, axis=3)
+            sub_full[0, h, c] = idx[0, h, c, :n]
+            ref = _dense_masked(q, kk, v, sub_full, vbs, scale)
+            np.testing.assert_allclose(out[0, rows, h], ref[0, rows, h], rtol=0, atol=1e-12)
+
+
+def test_lse_and_max_prob_against_dense_logsumexp():
+    """lse equals scipy's logsumexp over the brute-force masked score row, and
+    max_prob equals the largest entry of the dense softmax row."""
+    from scipy.special import logsumexp, softmax
+    rng = np.random.default_rng(11)
+    q, kk, v, vbs = _tiled_case(5, 6, 7, NH=1, D=16, B=1, rng=rng)
+    Nc = vbs.size
+    idx = _random_topk(1, 1, Nc, 3, rng=rng)
+    _, lse, mp = oracle.fwd_lut(q, kk, v, idx, None, vbs)
+    scale = 1 / math.sqrt(16)
+    S = Nc * 64
+    cube_of = np.arange(S) // 64
+    slot_of = np.arange(S) % 64
+    sel = np.zeros((Nc, Nc), bool)
+    for c in range(Nc):
+        sel[c, idx[0, 0, c]] = True
+    M = sel[cube_of][:, cube_of] & (slot_of < vbs[cube_of])[None, :]
+    s = np.where(M, q[0, :, 0] @ kk[0, :, 0].T * scale, -np.inf)
+    np.testing.assert_allclose(lse[0, 0], logsumexp(s, axis=1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mp[0, 0], softmax(s, axis=1).max(axis=1), rtol=1e-12, atol=0)
+
+
+def test_stats_closed_forms():
+    """One key: max_prob = 1 and lse = its scaled score. n keys with equal
+    scores: max_prob = 1/n and lse = s + log n."""
+    D = 8
+    vbs = np.array([1, 64, 0, 5], np.int32)
+    q = np.zeros((1, 4 * 64, 1, D))
+    k = np.zeros((1, 4 * 64, 1, D))
+    v = RNG.standard_normal((1, 4 * 64, 1, D))
+    q[0, :, 0, 0] = 1.0
+    k[0, 0, 0, 0] = 3.0                     # cube 0: one real token, score 3/sqrt(8)
+    k[0, 64:128, 0, 0] = 2.0                # cube 1: 64 equal scores 2/sqrt(8)
+    idx = np.array([[[[0, 1], [1, 2], [2, 3], [3, 0]]]], np.int32)
+    valid = np.array([[[1, 1, 1, 1]]], np.int32)
+    _, lse, mp = oracle.fwd_lut(q, k, v, idx, valid, vbs)
+    r = lambda c: slice(64 * c, 64 * (c + 1))
+    np.testing.assert_allclose(mp[0, 0, r(0)], 1.0, rtol=1e-15)
+    np.testing.assert_allclose(lse[0, 0, r(0)], 3 / math.sqrt(D), rtol=1e-15)
+    np.testing.assert_allclose(mp[0, 0, r(1)], 1 / 64, rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0, r(1)], 2 / math.sqrt(D) + math.log(64), rtol=1e-14)
+    assert np.all(np.isneginf(lse[0, 0, r(2)])) and np.all(mp[0, 0, r(2)] == 0)  # cube 2 empty
+    np.testing.assert_allclose(mp[0, 0, r(3)], 1 / 5, rtol=1e-14)   # 5 zero scores
+    np.testing.assert_allclose(lse[0, 0, r(3)], math.log(5), rtol=1e-14)

@@ -38,6 +38,8 @@ SIGNATURES = {
     "vsa_fwd_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "vsa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                          _c_int, ctypes.c_float, _vp, _sz, _vp]),
+    "vsa_fwd_lut": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                             _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _sz, _vp]),
     "vsa_validate_topk": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
 }
 

@@ -178,6 +178,43 @@ size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, i
   return vsa::fwd_workspace(B, Nq, Nkv, NH, D, topk).total;
 }
 
+namespace {
+// Shared argument checks and launch of vsa_fwd and vsa_fwd_lut.
+int32_t fwd_common(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                   const int32_t* idx, const int32_t* valid, const int32_t* vbs,
+                   vsa_bf16_t* out, float* lse, float* max_prob, int32_t B, int32_t Nq,
+                   int32_t Nkv, int32_t NH, int32_t D, int32_t row_len, float sm_scale,
+                   void* workspace, size_t workspace_bytes, vsa_stream_t stream) {
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  if (Nq <= 0 || Nkv <= 0) return fail(VSA_ERR_SHAPE, "Nq=%d Nkv=%d must be positive", Nq, Nkv);
+  if ((int64_t)B * NH * Nq > kMaxGridX)
+    return fail(VSA_ERR_SHAPE, "B*NH*Nq=%lld exceeds %lld", (long long)B * NH * Nq,
+                (long long)kMaxGridX);
+  if (row_len < 1 || row_len > Nkv)
+    return fail(VSA_ERR_RANGE, "index row length %d outside [1, %d]", row_len, Nkv);
+  if (!isfinite(sm_scale)) return fail(VSA_ERR_RANGE, "sm_scale is not finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(VSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  if (B > kMaxGridYZ) return fail(VSA_ERR_SHAPE, "B=%d exceeds %lld", B, (long long)kMaxGridYZ);
+  if ((uint64_t)Nkv * 64u * (uint64_t)NH * (uint64_t)D * 2u >= kMaxFwdKvBytes)
+    return fail(VSA_ERR_UNSUPPORTED, "Nkv * 64 * NH * D * 2 = %llu bytes per batch must be < 2^32",
+                (unsigned long long)Nkv * 64ull * NH * D * 2ull);
+  const size_t need = vsa::fwd_workspace(B, Nq, Nkv, NH, D, row_len).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(VSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_fwd(q, k, v, idx, valid, vbs, out, lse, max_prob, B, Nq, Nkv, NH,
+                                  D, row_len, sm_scale, workspace,
+                                  static_cast<hipStream_t>(stream)),
+                  "fwd");
+}
+}  // namespace
+
 int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
                 const int32_t* topk_idx, const int32_t* vbs, vsa_bf16_t* out, int32_t B,
                 int32_t Nq, int32_t Nkv, int32_t NH, int32_t D, int32_t topk,
@@ -186,31 +223,27 @@ int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
   if (q == nullptr || k == nullptr || v == nullptr || topk_idx == nullptr ||
       vbs == nullptr || out == nullptr)
     return fail(VSA_ERR_NULL, "q, k, v, topk_idx, vbs or out is NULL");
-  int32_t s = check_bhd(B, NH, D);
-  if (s != VSA_OK) return s;
-  if (Nq <= 0 || Nkv <= 0) return fail(VSA_ERR_SHAPE, "Nq=%d Nkv=%d must be positive", Nq, Nkv);
-  if ((int64_t)B * NH * Nq > kMaxGridX)
-    return fail(VSA_ERR_SHAPE, "B*NH*Nq=%lld exceeds %lld", (long long)B * NH * Nq,
-                (long long)kMaxGridX);
   if (topk < 1 || topk > Nkv) return fail(VSA_ERR_RANGE, "topk=%d outside [1, %d]", topk, Nkv);
-  if (!isfinite(sm_scale)) return fail(VSA_ERR_RANGE, "sm_scale is not finite");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(VSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
-  if (B > kMaxGridYZ) return fail(VSA_ERR_SHAPE, "B=%d exceeds %lld", B, (long long)kMaxGridYZ);
-  if ((uint64_t)Nkv * 64u * (uint64_t)NH * (uint64_t)D * 2u >= kMaxFwdKvBytes)
-    return fail(VSA_ERR_UNSUPPORTED, "Nkv * 64 * NH * D * 2 = %llu bytes per batch must be < 2^32",
-                (unsigned long long)Nkv * 64ull * NH * D * 2ull);
-  const size_t need = vsa::fwd_workspace(B, Nq, Nkv, NH, D, topk).total;
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(VSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
-  if ((s = check_device()) != VSA_OK) return s;
-  return launched(vsa::launch_fwd(q, k, v, topk_idx, vbs, out, B, Nq, Nkv, NH, D, topk,
-                                  sm_scale, workspace, static_cast<hipStream_t>(stream)),
-                  "fwd");
+  return fwd_common(q, k, v, topk_idx, nullptr, vbs, out, nullptr, nullptr, B, Nq, Nkv, NH, D,
+                    topk, sm_scale, workspace, workspace_bytes, stream);
+}
+
+int32_t vsa_fwd_lut(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                    const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                    const int32_t* vbs, vsa_bf16_t* out, float* lse, float* max_prob,
+                    int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                    int32_t max_kv, float sm_scale, void* workspace,
+                    size_t workspace_bytes, vsa_stream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr ||
+      vbs == nullptr || out == nullptr)
+    return fail(VSA_ERR_NULL, "q, k, v, kv_block_idx, vbs or out is NULL");
+  if (max_kv < 1 || max_kv > Nkv)
+    return fail(VSA_ERR_RANGE, "max_kv=%d outside [1, %d]", max_kv, Nkv);
+  if ((lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) ||
+      (max_prob != nullptr && (reinterpret_cast<uintptr_t>(max_prob) & 3u) != 0))
+    return fail(VSA_ERR_UNSUPPORTED, "lse and max_prob must be 4-byte aligned");
+  return fwd_common(q, k, v, kv_block_idx, valid_block_num, vbs, out, lse, max_prob, B, Nq,
+                    Nkv, NH, D, max_kv, sm_scale, workspace, workspace_bytes, stream);
 }
 
 int32_t vsa_validate_topk(const int32_t* topk_idx, int32_t B, int32_t NH, int32_t Nq,

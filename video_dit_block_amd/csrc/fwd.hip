@@ -218,8 +218,9 @@ __global__ __launch_bounds__(kCvtThreads) void v_to_fp16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Half-tile list pre-pass: one wave per unit (b, h, query cube). The selected
-// ids (clamped into range: a violated precondition gives unspecified values,
+// Half-tile list pre-pass: one wave per unit (b, h, query cube). The unit's
+// selected ids (the first valid[unit] entries of its index row, or all of
+// them; clamped into range: a violated precondition gives unspecified values,
 // never an out-of-bounds access) are sorted ascending and expanded into
 // 32-token half-tiles: half 0 of every cube with a real token, half 1 of
 // every cube with more than 32. Entry = (byte offset of the half from the
@@ -230,12 +231,14 @@ constexpr int kListSortCap = 1024;
 constexpr int kListPad = 4;
 
 __global__ __launch_bounds__(64) void halves_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ vbs,
-    uint32_t* __restrict__ list, int32_t* __restrict__ counts, int Nkv, int topk, int stride,
-    uint32_t rs2) {
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ valid,
+    const int32_t* __restrict__ vbs, uint32_t* __restrict__ list, int32_t* __restrict__ counts,
+    int Nkv, int row_len, int stride, uint32_t rs2) {
   __shared__ int32_t keys[kListSortCap];
   const int unit = blockIdx.x, lane = threadIdx.x;
-  const int32_t* __restrict__ sel = topk_idx + (size_t)unit * topk;
+  const int32_t* __restrict__ sel = topk_idx + (size_t)unit * row_len;
+  // the row's first `topk` ids are used: all of them, or valid[unit] (clamped)
+  const int topk = valid == nullptr ? row_len : min(max(valid[unit], 0), row_len);
   uint32_t* __restrict__ out = list + (size_t)unit * stride * 2;
   const bool sorted = topk <= kListSortCap;
   auto id_at = [&](int i) __attribute__((always_inline)) -> int {
@@ -291,8 +294,9 @@ template <int D>
 __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v16, const uint32_t* __restrict__ list,
-    const int32_t* __restrict__ counts, uint16_t* __restrict__ out, int Nq, int Nkv, int NH,
-    int list_stride, float scale_log2, int n_units) {
+    const int32_t* __restrict__ counts, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ max_prob, int Nq, int Nkv, int NH, int list_stride, float scale_log2,
+    int n_units) {
   using S = FwdShape<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][S::kHalfBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][S::kHalfBytes];
@@ -327,12 +331,16 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     return u32x2{(uint32_t)__builtin_amdgcn_readfirstlane((int)v[0]),
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)v[1])};
   };
+  // per-row statistics: row (b, h, c * 64 + 32 wave + qr), written by lane g = 0
+  const size_t srow = ((size_t)bh * Nq + qc) * kCube + 32 * wave + qr;
   if (n == 0) {  // no real key in any selected cube: the rows are 0
 #pragma unroll
     for (int db = 0; db < S::kDBlocks; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
         *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * r4 + 4 * g) = u32x2{0u, 0u};
+    if (g == 0 && lse != nullptr) lse[srow] = kNegInf;
+    if (g == 0 && max_prob != nullptr) max_prob[srow] = 0.0f;
     return;
   }
 
@@ -407,6 +415,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   // against; l_run: running sum of exp2((s - m_ref) * scale_log2); alpha and
   // need_rescale: the pending O rescale after a raise of m_ref
   float m_ref = kNegInf, l_run = 0.0f, alpha = 1.0f;
+  float m_row = kNegInf;  // the row's largest score so far (for max_prob)
   bool need_rescale = false;
   const floatx16 zero16 = {};
   const halfx2 ones = {(_Float16)1.0f, (_Float16)1.0f};
@@ -451,6 +460,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = halves_max(mx);
+    m_row = fmaxf(m_row, mx);
     const bool up = mx * scale_log2 > m_ref * scale_log2 + kRescaleThreshold;
     need_rescale = __builtin_amdgcn_ballot_w64(up) != 0;
     if (need_rescale) {
@@ -574,6 +584,15 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
       pv(0, pb, none, -1);
   }
 
+  // ---- per-row statistics. l_run sums exp2((s - m_ref) c), so the natural
+  // log-sum-exp of the scaled scores is (m_ref c + log2 l_run) ln 2, and the
+  // largest softmax weight is 1 / sum exp2((s - m_row) c) =
+  // exp2((m_row - m_ref) c) / l_run.
+  if (g == 0 && lse != nullptr)
+    lse[srow] = (m_ref * scale_log2 + __log2f(l_run)) * 0.69314718055994531f;
+  if (g == 0 && max_prob != nullptr)
+    max_prob[srow] = __builtin_amdgcn_exp2f((m_row - m_ref) * scale_log2) / l_run;
+
   // ---- epilogue: lane holds O^T[d][row] for d = 32 db + 8 (r/4) + 4 g + r%4
   const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
 #pragma unroll
@@ -601,9 +620,10 @@ FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk) {
 }
 
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      const int32_t* topk_idx, const int32_t* vbs, uint16_t* out,
-                      int B, int Nq, int Nkv, int NH, int D, int topk,
-                      float sm_scale, void* workspace, hipStream_t stream) {
+                      const int32_t* topk_idx, const int32_t* valid, const int32_t* vbs,
+                      uint16_t* out, float* lse, float* max_prob, int B, int Nq, int Nkv,
+                      int NH, int D, int topk, float sm_scale, void* workspace,
+                      hipStream_t stream) {
   const FwdWorkspace w = fwd_workspace(B, Nq, Nkv, NH, D, topk);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(ws + w.v16_off);
@@ -616,19 +636,19 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      cpr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(halves_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, vbs, list,
-                     counts, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u);
+  hipLaunchKernelGGL(halves_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, valid, vbs,
+                     list, counts, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   if (D == 128)
     hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_units), dim3(FwdShape<128>::kThreads), 0, stream,
-                       q, k, v16, list, counts, out, Nq, Nkv, NH, w.list_stride, scale_log2,
-                       n_units);
+                       q, k, v16, list, counts, out, lse, max_prob, Nq, Nkv, NH, w.list_stride,
+                       scale_log2, n_units);
   else
     hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_units), dim3(FwdShape<64>::kThreads), 0, stream,
-                       q, k, v16, list, counts, out, Nq, Nkv, NH, w.list_stride, scale_log2,
-                       n_units);
+                       q, k, v16, list, counts, out, lse, max_prob, Nq, Nkv, NH, w.list_stride,
+                       scale_log2, n_units);
   return hipGetLastError();
 }
 

@@ -33,10 +33,13 @@ struct FwdWorkspace {
   int list_stride;
 };
 FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk);
+// topk_idx rows hold `topk` ids; valid (may be NULL = all) gives the count
+// used per row; lse and max_prob (may be NULL) receive per-row statistics.
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      const int32_t* topk_idx, const int32_t* vbs, uint16_t* out,
-                      int B, int Nq, int Nkv, int NH, int D, int topk,
-                      float sm_scale, void* workspace, hipStream_t stream);
+                      const int32_t* topk_idx, const int32_t* valid, const int32_t* vbs,
+                      uint16_t* out, float* lse, float* max_prob, int B, int Nq, int Nkv,
+                      int NH, int D, int topk, float sm_scale, void* workspace,
+                      hipStream_t stream);
 
 hipError_t launch_validate_topk(const int32_t* topk_idx, int B, int NH, int Nq,
                                 int Nkv, int topk, int32_t* bad_count,

@@ -149,6 +149,53 @@ def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch
     return out
 
 
+def fwd_lut(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
+            kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor | None, vbs: torch.Tensor,
+            sm_scale: float | None = None, stats: bool = False,
+            workspace: torch.Tensor | None = None):
+    """Fine attention over the first valid_block_num[b, h, c] ids of each
+    kv_block_idx row (B, NH, Nq, max_kv); valid_block_num (B, NH, Nq) or None
+    for all. Returns out, or (out, lse, max_prob) with the per-row statistics
+    (B, NH, Nq*64) float32 when stats is true."""
+    for t, n in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
+        _bf16(t, n)
+    _i32(kv_block_idx, "kv_block_idx")
+    _i32(vbs, "vbs")
+    B, Sq, NH, D = q_t.shape
+    Skv = k_t.shape[1]
+    if v_t.shape != k_t.shape or k_t.shape[0] != B or k_t.shape[2:] != q_t.shape[2:]:
+        raise ValueError("k_t and v_t must be (B, Nkv*64, NH, D) matching q_t")
+    if Sq % CUBE or Skv % CUBE:
+        raise ValueError("sequence lengths must be multiples of 64")
+    Nq, Nkv = Sq // CUBE, Skv // CUBE
+    if kv_block_idx.dim() != 4 or tuple(kv_block_idx.shape[:3]) != (B, NH, Nq):
+        raise ValueError(f"kv_block_idx must be (B, NH, Nq, max_kv) = ({B}, {NH}, {Nq}, m)")
+    if valid_block_num is not None:
+        _i32(valid_block_num, "valid_block_num")
+        if tuple(valid_block_num.shape) != (B, NH, Nq):
+            raise ValueError(f"valid_block_num must be (B, NH, Nq) = ({B}, {NH}, {Nq})")
+    if vbs.numel() != Nkv:
+        raise ValueError(f"vbs must hold Nkv = {Nkv} entries")
+    max_kv = kv_block_idx.shape[3]
+    out = torch.empty_like(q_t)
+    lse = mp = None
+    if stats:
+        lse = torch.empty((B, NH, Sq), dtype=torch.float32, device=q_t.device)
+        mp = torch.empty((B, NH, Sq), dtype=torch.float32, device=q_t.device)
+    scale = 0.0 if sm_scale is None else float(sm_scale)
+    if workspace is None:
+        workspace = torch.empty(fwd_workspace_bytes(B, Nq, Nkv, NH, D, max_kv),
+                                dtype=torch.uint8, device=q_t.device)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _lib.check(_lib.load().vsa_fwd_lut(q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(),
+                                       kv_block_idx.data_ptr(), ptr(valid_block_num),
+                                       vbs.data_ptr(), out.data_ptr(), ptr(lse), ptr(mp), B, Nq,
+                                       Nkv, NH, D, max_kv, scale, workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream()),
+               "vsa_fwd_lut")
+    return (out, lse, mp) if stats else out
+
+
 def validate_topk(topk_idx: torch.Tensor, Nkv: int) -> int:
     """Number of out-of-range or repeated ids in topk_idx (B, NH, Nq, topk)."""
     _i32(topk_idx, "topk_idx")
