@@ -132,6 +132,33 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                    int32_t D, int32_t topk, int32_t* topk_idx, void* workspace,
                    size_t workspace_bytes, vsa_stream_t stream);
 
+/* Coarse selector with a cumulative-mass threshold (Optimizing block-sparse
+ * INT8 attention and multi-expert step caching for Wan 2.2, section
+ * "Decoupling Block Selection from Sparse CUDA Kernels": sort the block scores
+ * of each query block and keep key blocks by a cumulative distribution
+ * threshold). Scores S as for vsa_select; per row, with the scores sorted
+ * descending (equal scores by ascending id) as s_0 >= s_1 >= ... and
+ * w_i = exp((s_i - s_0) * sm_scale), Z = sum over all Nc cubes of w_i:
+ *   kv_block_idx[b,h,i,:]   the max_k leading ids of that order (the
+ *                           vsa_select result for topk = max_k)
+ *   valid_block_num[b,h,i]  the smallest n >= 1 with w_0 + ... + w_{n-1}
+ *                           >= tau * Z, capped at max_k
+ * The pair is the lookup table vsa_fwd_lut takes. The sums run in fp32 (a
+ * count can differ from an exact one where the cumulative mass is within
+ * fp32 rounding of tau * Z).
+ *   max_k            in [1, Nc]
+ *   tau              in (0, 1]
+ *   sm_scale         softmax scale of the scores; <= 0 selects 1/sqrt(D)
+ *   kv_block_idx     [B][NH][Nc][max_k] int32 device output
+ *   valid_block_num  [B][NH][Nc] int32 device output
+ * Other arguments and the workspace as for vsa_select. Errors: as for
+ * vsa_select. */
+int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                       const int32_t* vbs, int32_t B, int32_t Nc, int32_t NH, int32_t D,
+                       int32_t max_k, float tau, float sm_scale, int32_t* kv_block_idx,
+                       int32_t* valid_block_num, void* workspace, size_t workspace_bytes,
+                       vsa_stream_t stream);
+
 /* Bytes of device workspace vsa_fwd needs for these sizes: an fp16 copy of v
  * in the tiled layout (B * Nkv * 64 * NH * D * 2 bytes), then, per (b, h,
  * query cube) (B * NH * Nq of them), the list of the 32-token halves that

@@ -26,6 +26,12 @@ What it computes, and where the pages define it:
   "Optimizing block-sparse INT8 attention and multi-expert step caching for
   Wan 2.2", section "Decoupling Block Selection from Sparse CUDA Kernels"
   (mean-pool summaries, dot-product block scores).
+* ``select_cdf`` -- the selector with a cumulative-mass threshold: per row the
+  cubes in score order, and the count of leading cubes whose softmax mass
+  (scores times sm_scale) first reaches tau, capped at max_k.
+  Pages: Wan INT8 blog, section "Decoupling Block Selection from Sparse CUDA
+  Kernels" (sort the block scores per query block, keep key blocks by a
+  cumulative distribution threshold).
 * ``fwd`` -- the fine stage: for every (batch, head, query cube) and each of
   its 64 rows, softmax((q . K_sel^T) / sqrt(D)) . V_sel over the real tokens of
   the selected key/value cubes.
@@ -56,6 +62,9 @@ the design notes of the repository):
 10. A row whose selected cubes hold no real token outputs 0 (and, in
     ``fwd_lut``, lse = -inf and max_prob = 0).
 11. The log-sum-exp is natural-log, over the scaled scores sm_scale q.k_j.
+12. The cumulative distribution of ``select_cdf`` is that of the softmax of
+    the row's cube scores times sm_scale (default 1/sqrt(D)); the count is the
+    smallest n >= 1 whose leading n cubes hold at least tau of the mass.
 """
 from __future__ import annotations
 
@@ -76,6 +85,8 @@ __all__ = [
     "cube_scores",
     "topk_select",
     "select",
+    "cdf_counts",
+    "select_cdf",
     "fwd_unit",
     "fwd",
     "fwd_units",
@@ -271,6 +282,31 @@ def select(q_t: np.ndarray, k_t: np.ndarray, vbs: np.ndarray, k: int):
 
 
 # --------------------------------------------------------------- fine stage
+
+def cdf_counts(S: np.ndarray, max_k: int, tau: float, scale: float):
+    """Wan INT8 blog, "Decoupling Block Selection": sort each row's scores
+    (descending, ties by ascending id, as ``topk_select``), take the softmax
+    weights w_i = exp((s_i - s_0) * scale) in that order and keep the fewest
+    leading cubes whose share of the total weight reaches tau.
+    Returns (ids (..., max_k), counts (...)), the counts capped at max_k."""
+    assert 0.0 < tau <= 1.0
+    order = topk_select(S, S.shape[-1])
+    ss = np.take_along_axis(np.asarray(S, np.float64), order.astype(np.int64), axis=-1)
+    w = np.exp((ss - ss[..., :1]) * scale)
+    c = np.cumsum(w, axis=-1)
+    n = np.argmax(c >= tau * c[..., -1:], axis=-1) + 1
+    return order[..., :max_k], np.minimum(n, max_k).astype(np.int32)
+
+
+def select_cdf(q_t: np.ndarray, k_t: np.ndarray, vbs: np.ndarray, max_k: int, tau: float,
+               sm_scale: float | None = None):
+    """Coarse selector with a cumulative-mass threshold: (ids, counts, S)."""
+    D = q_t.shape[-1]
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    S = cube_scores(mean_pool(q_t, vbs), mean_pool(k_t, vbs))
+    ids, n = cdf_counts(S, max_k, tau, scale)
+    return ids, n, S
+
 
 def _selected_rows(sel: np.ndarray, vbs: np.ndarray) -> np.ndarray:
     """Tiled row indices of the real tokens of the selected cubes."""

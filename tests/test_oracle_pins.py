@@ -454,3 +454,48 @@ def test_stats_closed_forms():
     assert np.all(np.isneginf(lse[0, 0, r(2)])) and np.all(mp[0, 0, r(2)] == 0)  # cube 2 empty
     np.testing.assert_allclose(mp[0, 0, r(3)], 1 / 5, rtol=1e-14)   # 5 zero scores
     np.testing.assert_allclose(lse[0, 0, r(3)], math.log(5), rtol=1e-14)
+
+
+# ------------------------------------------------ cumulative-mass selector
+
+def test_cdf_counts_constructed_weights():
+    """Scores log(8), log(4), log(2), 0, 0 at scale 1 give weights 8, 4, 2, 1, 1
+    (total 16): cumulative shares 0.5, 0.75, 0.875, 0.9375, 1."""
+    S = np.array([[0.0, math.log(2), math.log(8), 0.0, math.log(4)]])
+    for tau, n in [(0.3, 1), (0.5, 1), (0.51, 2), (0.75, 2), (0.76, 3), (0.875, 3),
+                   (0.9, 4), (0.95, 5), (1.0, 5)]:
+        ids, cnt = oracle.cdf_counts(S, 5, tau, 1.0)
+        assert cnt[0] == n, (tau, cnt[0], n)
+        assert list(ids[0]) == [2, 4, 1, 0, 3]   # descending, ties by lower id
+    _, cnt = oracle.cdf_counts(S, 2, 0.99, 1.0)
+    assert cnt[0] == 2                            # capped at max_k
+
+
+def test_cdf_counts_uniform_rows_and_monotone():
+    N = 37
+    S = np.full((3, N), 1.5)
+    for tau in (0.1, 0.33, 0.5, 0.8, 1.0):
+        _, cnt = oracle.cdf_counts(S, N, tau, 0.7)
+        assert np.all(cnt == math.ceil(round(tau * N, 9))), (tau, cnt)
+    rng = np.random.default_rng(5)
+    S = rng.standard_normal((20, 50)) * 3
+    prev = np.zeros(20, np.int32)
+    for tau in np.linspace(0.05, 1.0, 20):
+        ids, cnt = oracle.cdf_counts(S, 50, tau, 0.5)
+        assert np.all(cnt >= prev) and np.all((cnt >= 1) & (cnt <= 50))
+        prev = cnt
+        np.testing.assert_array_equal(ids, oracle.topk_select(S, 50))
+
+
+def test_cdf_counts_brute_force_definition():
+    """The count is the smallest n whose leading weights reach tau of the total,
+    checked by direct summation over each candidate n."""
+    rng = np.random.default_rng(8)
+    S = rng.standard_normal((30, 12)) * 2
+    for tau in (0.2, 0.6, 0.9, 0.999):
+        ids, cnt = oracle.cdf_counts(S, 12, tau, 1.3)
+        for r in range(S.shape[0]):
+            w = [math.exp((S[r, j] - S[r].max()) * 1.3) for j in ids[r]]
+            total = math.fsum(w)
+            n = next(n for n in range(1, 13) if math.fsum(w[:n]) >= tau * total - 1e-12 * total)
+            assert cnt[r] == n, (tau, r, cnt[r], n)

@@ -169,7 +169,43 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
     return fail(VSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if ((s = check_device()) != VSA_OK) return s;
   return launched(vsa::launch_select(q_tiled, k_tiled, vbs, B, Nc, NH, D, topk, topk_idx,
-                                     workspace, static_cast<hipStream_t>(stream)), "select");
+                                     nullptr, 0.0f, 0.0f, workspace,
+                                     static_cast<hipStream_t>(stream)),
+                  "select");
+}
+
+int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                       const int32_t* vbs, int32_t B, int32_t Nc, int32_t NH, int32_t D,
+                       int32_t max_k, float tau, float sm_scale, int32_t* kv_block_idx,
+                       int32_t* valid_block_num, void* workspace, size_t workspace_bytes,
+                       vsa_stream_t stream) {
+  if (valid_block_num == nullptr) return fail(VSA_ERR_NULL, "valid_block_num is NULL");
+  if (!(tau > 0.0f && tau <= 1.0f)) return fail(VSA_ERR_RANGE, "tau must be in (0, 1]");
+  if (!isfinite(sm_scale)) return fail(VSA_ERR_RANGE, "sm_scale is not finite");
+  if (q_tiled == nullptr || k_tiled == nullptr || vbs == nullptr || kv_block_idx == nullptr)
+    return fail(VSA_ERR_NULL, "q_tiled, k_tiled, vbs or kv_block_idx is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  if (Nc <= 0) return fail(VSA_ERR_SHAPE, "Nc=%d must be positive", Nc);
+  if (Nc > VSA_MAX_CUBES)
+    return fail(VSA_ERR_UNSUPPORTED, "Nc=%d exceeds VSA_MAX_CUBES=%d", Nc, VSA_MAX_CUBES);
+  if ((int64_t)B * NH > kMaxGridYZ)
+    return fail(VSA_ERR_SHAPE, "B*NH=%lld exceeds %lld", (long long)B * NH, (long long)kMaxGridYZ);
+  if (max_k < 1 || max_k > Nc) return fail(VSA_ERR_RANGE, "max_k=%d outside [1, %d]", max_k, Nc);
+  if (!aligned16(q_tiled) || !aligned16(k_tiled))
+    return fail(VSA_ERR_UNSUPPORTED, "q_tiled and k_tiled must be 16-byte aligned");
+  const size_t need = vsa::select_workspace(B, NH, Nc, D).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(VSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_select(q_tiled, k_tiled, vbs, B, Nc, NH, D, max_k, kv_block_idx,
+                                     valid_block_num, sm_scale, tau, workspace,
+                                     static_cast<hipStream_t>(stream)),
+                  "select_cdf");
 }
 
 size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,

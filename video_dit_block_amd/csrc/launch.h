@@ -20,10 +20,11 @@ struct SelectWorkspace {
 };
 SelectWorkspace select_workspace(int B, int NH, int Nc, int D);
 
+// valid != nullptr: also write the CDF count per row (scale, tau).
 hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          const int32_t* vbs, int B, int Nc, int NH, int D,
-                         int topk, int32_t* topk_idx, void* workspace,
-                         hipStream_t stream);
+                         int topk, int32_t* topk_idx, int32_t* valid, float scale, float tau,
+                         void* workspace, hipStream_t stream);
 
 // Workspace carve-up of vsa_fwd: an fp16 copy of v in the tiled layout, the
 // half-tile lists of the query-cube pairs ([B*NH*ceil(Nq/2)][list_stride]

@@ -21,6 +21,11 @@
 //                 (order-preserving score bits, then the complemented cube id)
 //                 in LDS, descending; the first topk ids are written out.
 //                 Equal scores therefore come out by ascending cube id.
+//                 With a CDF threshold tau it also writes the row's count: the
+//                 fewest leading cubes whose softmax mass (softmax over all Nc
+//                 scores times `scale`) reaches tau, capped at topk (Wan INT8
+//                 blog, same section: sort block scores per query block and
+//                 keep key blocks by a cumulative distribution threshold).
 #include "device.h"
 #include "launch.h"
 
@@ -146,12 +151,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key.
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // grid (Nc rows, B*NH). Dynamic LDS: n_pow2 * 8 bytes.
 // Key = order_key(score) << 32 | (0xFFFFFFFF - j). Real keys are > 0; the
-// padding keys (0) sort below every real key.
+// padding keys (0) sort below every real key. valid != nullptr selects the
+// CDF count (scale, tau).
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float* __restrict__ s, int32_t* __restrict__ topk_idx, int Nc,
-    int n_pow2, int topk) {
+    int n_pow2, int topk, int32_t* __restrict__ valid, float scale, float tau) {
   extern __shared__ uint64_t keys[];
   const size_t row = (size_t)blockIdx.y * Nc + blockIdx.x;
   const float* __restrict__ srow = s + row * Nc;
@@ -180,6 +191,44 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   int32_t* __restrict__ out = topk_idx + row * topk;
   for (int t = threadIdx.x; t < topk; t += kTopkThreads)
     out[t] = (int32_t)(0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull));
+  if (valid == nullptr) return;
+
+  // ---- CDF count. Weights w_i = exp((s_i - s_0) scale) over the sorted
+  // scores (s_0 the row max), Z = sum_i w_i; the count is the smallest n with
+  // w_0 + ... + w_{n-1} >= tau Z, at most topk. Thread t owns the ranks
+  // [t per, t per + per); a scan of the per-thread sums gives every thread
+  // its running sum at the start of its ranks.
+  __shared__ float part[kTopkThreads];
+  __shared__ int first;
+  const int tid = threadIdx.x;
+  const int per = (Nc + kTopkThreads - 1) / kTopkThreads;
+  const int r0 = tid * per, r1 = min(r0 + per, Nc);
+  const float s0 = key_score((uint32_t)(keys[0] >> 32));
+  auto w = [&](int i) __attribute__((always_inline)) -> float {
+    return __expf((key_score((uint32_t)(keys[i] >> 32)) - s0) * scale);
+  };
+  float loc = 0.0f;
+  for (int i = r0; i < r1; ++i) loc += w(i);
+  part[tid] = loc;
+  if (tid == 0) first = 0x7FFFFFFF;
+  __syncthreads();
+  for (int off = 1; off < kTopkThreads; off <<= 1) {  // inclusive scan
+    const float add = tid >= off ? part[tid - off] : 0.0f;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  const float thr = tau * part[kTopkThreads - 1];
+  float run = tid > 0 ? part[tid - 1] : 0.0f;
+  for (int i = r0; i < r1; ++i) {
+    run += w(i);
+    if (run >= thr) {
+      atomicMin(&first, i);
+      break;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) valid[row] = first == 0x7FFFFFFF ? min(Nc, topk) : min(first + 1, topk);
 }
 
 }  // namespace
@@ -196,8 +245,8 @@ SelectWorkspace select_workspace(int B, int NH, int Nc, int D) {
 
 hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          const int32_t* vbs, int B, int Nc, int NH, int D,
-                         int topk, int32_t* topk_idx, void* workspace,
-                         hipStream_t stream) {
+                         int topk, int32_t* topk_idx, int32_t* valid, float scale, float tau,
+                         void* workspace, hipStream_t stream) {
   const SelectWorkspace w = select_workspace(B, NH, Nc, D);
   char* ws = static_cast<char*>(workspace);
   float* qc = reinterpret_cast<float*>(ws + w.qc_off);
@@ -224,7 +273,7 @@ hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
   if (n_pow2 < 2) n_pow2 = 2;
   hipLaunchKernelGGL(topk_kernel, dim3(Nc, B * NH), dim3(kTopkThreads),
                      (size_t)n_pow2 * sizeof(uint64_t), stream, s, topk_idx, Nc,
-                     n_pow2, topk);
+                     n_pow2, topk, valid, scale, tau);
   return hipGetLastError();
 }
 

@@ -110,6 +110,32 @@ def select(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk: int,
     return out
 
 
+def select_cdf(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, max_k: int, tau: float,
+               sm_scale: float | None = None, workspace: torch.Tensor | None = None):
+    """Coarse selector with a cumulative softmax-mass threshold: returns
+    (kv_block_idx int32 (B, NH, Nc, max_k), valid_block_num int32 (B, NH, Nc))."""
+    _bf16(q_t, "q_t")
+    _bf16(k_t, "k_t")
+    _i32(vbs, "vbs")
+    B, S, NH, D = q_t.shape
+    Nc = S // CUBE
+    if k_t.shape != q_t.shape or S % CUBE:
+        raise ValueError("q_t and k_t must both be (B, Nc*64, NH, D)")
+    if workspace is None:
+        workspace = torch.empty(select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8,
+                                device=q_t.device)
+    idx = torch.empty((B, NH, Nc, max_k), dtype=torch.int32, device=q_t.device)
+    valid = torch.empty((B, NH, Nc), dtype=torch.int32, device=q_t.device)
+    scale = 0.0 if sm_scale is None else float(sm_scale)
+    _lib.check(_lib.load().vsa_select_cdf(q_t.data_ptr(), k_t.data_ptr(), vbs.data_ptr(), B, Nc,
+                                          NH, D, max_k, float(tau), scale, idx.data_ptr(),
+                                          valid.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream()),
+               "vsa_select_cdf")
+    return idx, valid
+
+
 def fwd_workspace_bytes(B: int, Nq: int, Nkv: int, NH: int, D: int, topk: int) -> int:
     return int(_lib.load().vsa_fwd_workspace_bytes(B, Nq, Nkv, NH, D, topk))
 
