@@ -58,6 +58,13 @@ def fwd_flops(topk_idx: np.ndarray, vbs: np.ndarray, D: int) -> float:
     return 4.0 * D * 64.0 * float(sel_tokens)
 
 
+def lut_flops(kv_block_idx: np.ndarray, counts: np.ndarray, vbs: np.ndarray, D: int) -> float:
+    """fwd_flops over the first counts[b, h, c] ids of each row."""
+    used = np.arange(kv_block_idx.shape[-1]) < counts[..., None]
+    sel_tokens = (vbs[kv_block_idx].astype(np.int64) * used).sum()
+    return 4.0 * D * 64.0 * float(sel_tokens)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,6 +76,8 @@ def parse():
     ap.add_argument("--hy720", action="store_true",
                     help="also time the whole path on the 720p HunyuanVideo-like workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cdf-tau", type=float, default=0.9,
+                    help="threshold of the cumulative-mass selector leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only vsa_fwd launches (for profiler runs)")
@@ -302,7 +311,83 @@ def main():
             sweep[str(kk)] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
                               "speedup_vs_dense": round(dense_ms / ms, 3)}
         del ik
-    del idx_all, out_d
+    del idx_all
+
+    # lookup-table leg: the cumulative-mass selector (tau, at most half of the
+    # cubes) and vsa_fwd_lut on its table, with and without the row statistics
+    max_k = Nc // 2
+    lidx, lcnt = vsa.select_cdf(qt, kt, vbs, max_k, args.cdf_tau, workspace=ws)
+    lse = torch.empty((B, NH, S), dtype=torch.float32, device=dev)
+    mp = torch.empty_like(lse)
+    lib = vsa._lib.load()
+    ptrs = lambda o, st: (qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), lidx.data_ptr(),
+                          lcnt.data_ptr(), vbs.data_ptr(), o.data_ptr(),
+                          lse.data_ptr() if st else None, mp.data_ptr() if st else None,
+                          B, Nc, Nc, NH, D, max_k, 0.0, wsf.data_ptr(), wsf.numel(),
+                          torch.cuda.current_stream().cuda_stream)
+    timed = {}
+    for name, fn in (("select_cdf", lambda: vsa.select_cdf(qt, kt, vbs, max_k, args.cdf_tau,
+                                                           workspace=ws)),
+                     ("fwd_lut", lambda: lib.vsa_fwd_lut(*ptrs(out_d, False))),
+                     ("fwd_lut_stats", lambda: lib.vsa_fwd_lut(*ptrs(out_d, True)))):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps_d):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        timed[name] = e0.elapsed_time(e1) / reps_d
+    lcnt_h = lcnt.cpu().numpy()
+    lfl = lut_flops(lidx.cpu().numpy(), lcnt_h, vbs_h, D)
+    lut = {"tau": args.cdf_tau, "max_k": max_k, "mean_count": round(float(lcnt_h.mean()), 2),
+           "sparsity": round(1 - float(lcnt_h.mean()) / Nc, 4),
+           "select_cdf_ms": round(timed["select_cdf"], 4),
+           "fwd_lut_ms": round(timed["fwd_lut"], 4), "fwd_lut_tflop": round(lfl / 1e12, 4),
+           "fwd_lut_tflops": round(lfl / timed["fwd_lut"] / 1e9, 1),
+           "fwd_lut_with_lse_max_prob_ms": round(timed["fwd_lut_stats"], 4),
+           "stats_finite": bool(torch.isfinite(lse).all() and torch.isfinite(mp).all())}
+    del out_d, lidx, lcnt, lse, mp
+
+    # two-stage leg: the coarse stage's own output (pooled q, k, v, cube scores,
+    # softmax over cubes times pooled v), with and without the top-k ids taken
+    # from the same scores, and the gated combine with seeded uniform gates
+    wsc = torch.empty(vsa.coarse_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8, device=dev)
+    oc = torch.empty((B, NH, Nc, D), dtype=torch.float32, device=dev)
+    idx2 = torch.empty_like(idx)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    gc = torch.rand(tuple(qt.shape), device=dev, generator=gen).to(torch.bfloat16)
+    gf = torch.rand(tuple(qt.shape), device=dev, generator=gen).to(torch.bfloat16)
+    comb = torch.empty_like(qt)
+    stream = torch.cuda.current_stream().cuda_stream
+    cargs = lambda ids: (qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), vbs.data_ptr(), B, Nc, NH,
+                         D, topk, ids, 0.0, oc.data_ptr(), wsc.data_ptr(), wsc.numel(), stream)
+    for name, fn in (("coarse", lambda: lib.vsa_coarse(*cargs(None))),
+                     ("coarse_topk", lambda: lib.vsa_coarse(*cargs(idx2.data_ptr()))),
+                     ("combine", lambda: lib.vsa_gate_combine(out.data_ptr(), oc.data_ptr(),
+                                                              gc.data_ptr(), gf.data_ptr(),
+                                                              comb.data_ptr(), B, Nc, NH, D,
+                                                              stream))):
+        assert fn() == 0, name
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps_d):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        timed[name] = e0.elapsed_time(e1) / reps_d
+    comb_bytes = 4 * S * NH * D * 2 + oc.numel() * 4
+    two_stage = {
+        "coarse_ms": round(timed["coarse"], 4),
+        "coarse_with_topk_ms": round(timed["coarse_topk"], 4),
+        "topk_equal_to_select": bool(torch.equal(idx2, idx)),
+        "gate_combine_ms": round(timed["combine"], 4),
+        "gate_combine_gbs": round(comb_bytes / (timed["combine"] * 1e-3) / 1e9, 1),
+        "o_coarse_finite": bool(torch.isfinite(oc).all()),
+        "step_ms": round(parts[0] + timed["coarse_topk"] + parts[2] + timed["combine"] + parts[3],
+                         4),
+    }
+    del wsc, oc, idx2, gc, gf, comb
 
     # tiling traffic: read real rows, write all rows, per tensor
     tile_bytes = 3 * (T * H * W + S) * NH * D * 2
@@ -345,6 +430,8 @@ def main():
                      "traffic": profiled_traffic()},
         "cpu_baseline": cpu,
     }
+    line["lut"] = lut
+    line["two_stage"] = two_stage
     if sweep is not None:
         line["sweep"] = sweep
     if args.hy720:

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 2
+#define VSA_ABI_VERSION 3
 #define VSA_CUBE 64
 
 typedef uint16_t vsa_bf16_t; /* raw bf16 bits */
@@ -236,6 +236,61 @@ int32_t vsa_fwd_lut(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* 
                     int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
                     int32_t max_kv, float sm_scale, void* workspace,
                     size_t workspace_bytes, vsa_stream_t stream);
+
+/* Bytes of device workspace vsa_coarse needs: the vsa_select workspace
+ * (pooled q and k, the scores) followed by the pooled v (B * NH * Nc * D
+ * float32), each part 256-byte aligned. Returns 0 for invalid sizes. */
+size_t vsa_coarse_workspace_bytes(int32_t B, int32_t NH, int32_t Nc, int32_t D);
+
+/* Coarse stage: attention among mean-pooled cubes, and optionally the top-k
+ * selection from the same scores. VSA blog, "Two-Stage Architecture": Stage 1
+ * pools each cube, scores cube against cube and keeps the Top-K key cubes per
+ * query cube; the final output also uses the coarse stage's own output.
+ * For each (b, h), with Qc, Kc, Vc the means over the real rows of each cube
+ * of q_tiled, k_tiled, v_tiled (as in vsa_select) and S = Qc . Kc^T:
+ *   o_coarse[b][h][i][:] = sum_j softmax_j(S[i][j] * sm_scale) Vc[j][:]
+ * with j over the key cubes whose vbs[j] > 0 (all weights are 0, and the row
+ * is 0, when there is none). Everything runs in fp32.
+ *   q_tiled, k_tiled, v_tiled  [B][Nc*64][NH][D] bf16, tiled order
+ *   vbs       [Nc] int32, each in [0, 64]
+ *   topk      ids per row written to topk_idx, in [1, Nc]; ignored when
+ *             topk_idx is NULL
+ *   topk_idx  [B][NH][Nc][topk] int32 device output or NULL; when given it is
+ *             exactly what vsa_select writes for the same inputs
+ *   sm_scale  softmax scale of the coarse scores; <= 0 selects 1/sqrt(D);
+ *             must be finite
+ *   o_coarse  [B][NH][Nc][D] float32 device output
+ *   workspace >= vsa_coarse_workspace_bytes(B, NH, Nc, D) bytes, 256-byte
+ *             aligned, not overlapping the tensors; on return it holds Qc, Kc,
+ *             S and Vc (layout not part of the interface)
+ * q_tiled, k_tiled, v_tiled and o_coarse must be 16-byte aligned. Errors:
+ * VSA_ERR_NULL, VSA_ERR_SHAPE, VSA_ERR_UNSUPPORTED (D, alignment, Nc >
+ * VSA_MAX_CUBES), VSA_ERR_RANGE (topk, sm_scale), VSA_ERR_WORKSPACE,
+ * VSA_ERR_HIP. */
+int32_t vsa_coarse(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                   const vsa_bf16_t* v_tiled, const int32_t* vbs, int32_t B, int32_t Nc,
+                   int32_t NH, int32_t D, int32_t topk, int32_t* topk_idx, float sm_scale,
+                   float* o_coarse, void* workspace, size_t workspace_bytes,
+                   vsa_stream_t stream);
+
+/* Gated combine of the two stages. VSA blog, "Two-Stage Architecture" (the
+ * final output mixes the coarse-stage and fine-stage outputs through
+ * learnable gates). For every token row s of cube c = s / 64, head h and
+ * channel d:
+ *   out[b][s][h][d] = bf16(gate_coarse[b][s][h][d] * o_coarse[b][h][c][d]
+ *                          + gate_fine[b][s][h][d] * o_fine[b][s][h][d])
+ * evaluated in fp32 (one fused multiply-add over the fine product) and
+ * rounded to nearest even.
+ *   o_fine, gate_coarse, gate_fine, out  [B][Nc*64][NH][D] bf16, tiled order;
+ *             out may be the same buffer as o_fine or as a gate (each element
+ *             is read before it is written), otherwise no overlap
+ *   o_coarse  [B][NH][Nc][D] float32 (vsa_coarse's output)
+ * All pointers must be 16-byte aligned. Errors: VSA_ERR_NULL, VSA_ERR_SHAPE,
+ * VSA_ERR_UNSUPPORTED, VSA_ERR_HIP. */
+int32_t vsa_gate_combine(const vsa_bf16_t* o_fine, const float* o_coarse,
+                         const vsa_bf16_t* gate_coarse, const vsa_bf16_t* gate_fine,
+                         vsa_bf16_t* out, int32_t B, int32_t Nc, int32_t NH, int32_t D,
+                         vsa_stream_t stream);
 
 /* Checks the vsa_fwd precondition on topk_idx on the device: counts, into
  * *bad_count (one int32 in device memory, which the caller zeroes first), the

@@ -45,6 +45,15 @@ What it computes, and where the pages define it:
   entries); Wan INT8 blog, "Dynamic Sparsity Budgeting via Softmax
   Normalizer Registers" (max_prob = 1 / l_i).
 
+* ``coarse_output`` / ``gated_combine`` -- the coarse stage's own output,
+  attention among the mean-pooled cubes softmax(Qc Kc^T * sm_scale) Vc per
+  (batch, head), and the layer output that mixes it with the fine output
+  through gates: out = g_c * Oc[cube of the row] + g_f * O_fine.
+  Pages: VSA blog, "Two-Stage Architecture" (Stage 1 works on mean-pooled
+  cubes; the final output combines the coarse-stage and fine-stage outputs
+  through learnable gates) and its VSA/Jenga comparison (a learnable gate
+  between coarse and fine).
+
 Readings where the pages are silent (each one is listed with its reason in
 the design notes of the repository):
 
@@ -65,6 +74,12 @@ the design notes of the repository):
 12. The cumulative distribution of ``select_cdf`` is that of the softmax of
     the row's cube scores times sm_scale (default 1/sqrt(D)); the count is the
     smallest n >= 1 whose leading n cubes hold at least tau of the mass.
+13. The coarse output is dense attention of every pooled query cube over the
+    pooled key cubes that hold a real token (vbs[j] > 0), with sm_scale
+    (default 1/sqrt(D)); a row with no such key cube is 0. It is broadcast to
+    the 64 rows of its cube.
+14. The gates are given tensors of the output's shape, applied elementwise;
+    how a model computes them (learned projections) is outside the path.
 """
 from __future__ import annotations
 
@@ -92,6 +107,8 @@ __all__ = [
     "fwd_units",
     "fwd_unit_stats",
     "fwd_lut",
+    "coarse_output",
+    "gated_combine",
 ]
 
 #: tokens per cube edge (the VSA blog: (Ct, Ch, Cw) = (4, 4, 4))
@@ -413,3 +430,44 @@ def fwd_lut(q_t, k_t, v_t, kv_block_idx, valid_block_num, vbs, sm_scale=None):
                 lse[b, h, c * CUBE:(c + 1) * CUBE] = e
                 mp[b, h, c * CUBE:(c + 1) * CUBE] = x
     return out, lse, mp
+
+
+# ------------------------------------------------------ coarse output, combine
+
+def coarse_output(q_t, k_t, v_t, vbs, sm_scale=None) -> np.ndarray:
+    """Coarse-stage output Oc (B, NH, Nc, D), float64.
+
+    VSA blog, "Two-Stage Architecture": the coarse stage attends among the
+    mean-pooled cubes. Per (b, h): Oc = softmax(Qc Kc^T * sm_scale) Vc with Qc,
+    Kc, Vc from ``mean_pool``, the softmax over the key cubes with vbs[j] > 0
+    (reading 13).
+    """
+    D = q_t.shape[-1]
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    vbs = np.asarray(vbs)
+    Qc, Kc, Vc = mean_pool(q_t, vbs), mean_pool(k_t, vbs), mean_pool(v_t, vbs)
+    real = vbs > 0
+    B, NH, Nc, _ = Qc.shape
+    out = np.zeros((B, NH, Nc, D))
+    if not real.any():
+        return out
+    for b in range(B):
+        for h in range(NH):
+            s = (Qc[b, h] @ Kc[b, h][real].T) * scale          # (Nc, n_real)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[b, h] = (p @ Vc[b, h][real]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def gated_combine(o_fine, o_coarse, gate_coarse, gate_fine) -> np.ndarray:
+    """out[b, s, h, :] = gate_coarse[b, s, h, :] * Oc[b, h, s // 64, :]
+    + gate_fine[b, s, h, :] * o_fine[b, s, h, :], float64 (B, Nc*64, NH, D).
+
+    VSA blog, "Two-Stage Architecture": the final output mixes the coarse-stage
+    and fine-stage outputs through gates (reading 14: elementwise tensors).
+    """
+    o_coarse = np.asarray(o_coarse, np.float64)
+    B, NH, Nc, D = o_coarse.shape
+    oc_rows = np.repeat(np.transpose(o_coarse, (0, 2, 1, 3)), CUBE, axis=1)  # (B, Nc*64, NH, D)
+    return (np.asarray(gate_coarse, np.float64) * oc_rows
+            + np.asarray(gate_fine, np.float64) * np.asarray(o_fine, np.float64))

@@ -214,3 +214,70 @@ class ConfigRun:
         for b, h, cc in units:
             by_head.setdefault(h, []).append(out_bits[b, 64 * cc:64 * (cc + 1), h])
         return {h: np.stack(v) for h, v in by_head.items()}
+
+
+def coarse_tolerance(Qc, Kc, Vc, Qa, Ka, Va, vbs, scale, n_pool: int = 64):
+    """Per (i, d) bound on |device o_coarse - oracle| for one (b, h), from the
+    kernels' fp32 arithmetic (u = 2^-24):
+    * pooled means are off by <= gamma_{n+1} times the mean of |x|;
+    * score S_ij = Qc_i . Kc_j is then off by <= e_ij = gamma_D |Qc_i|.|Kc_j|
+      + gamma_{n+1} (Qa_i.|Kc_j| + |Qc_i|.Ka_j); e_i = max over real j;
+    * weight exp2((S_ij - m_i) scale log2 e): relative error <= delta_i =
+      (2 e_i + 6 u max_j |S_ij|) scale + 2^-22 (argument roundings, the
+      hardware exp2);
+    * normalisation and the Nc-term fp32 sums add (2 Nc + 4) u relative;
+    so |dO_id| <= (2 delta_i + (2 Nc + 4) u) max_j |Vc_jd| + gamma_{n+1}
+    max_j Va_jd. Qc.. are (Nc, D) float64; the maxima run over key cubes with
+    vbs > 0."""
+    real = np.asarray(vbs) > 0
+    Nc, D = Qc.shape
+    aQ, aK = np.abs(Qc), np.abs(Kc)
+    g = gamma(n_pool + 1)
+    e = gamma(D) * aQ @ aK.T + g * (Qa @ aK.T + aQ @ Ka.T)
+    e_i = e[:, real].max(axis=1)
+    smax = np.abs(Qc @ Kc.T)[:, real].max(axis=1)
+    delta = (2 * e_i + 6 * U32 * smax) * scale + 2.0 ** -22
+    vmax = np.abs(Vc[real]).max(axis=0)
+    return (2 * delta + (2 * Nc + 4) * U32)[:, None] * vmax[None, :] + g * Va[real].max(axis=0)[None, :]
+
+
+def check_coarse(oc_gpu: np.ndarray, head64, vbs, NH: int, sm_scale, label: str) -> float:
+    """Every element of o_coarse (B, NH, Nc, D) against the oracle. head64(name,
+    h) returns the tiled float64 tensor `name` of head h as (B, S, 1, D).
+    Returns the worst error / bound ratio."""
+    B, _, Nc, D = oc_gpu.shape
+    scale = 1.0 / math.sqrt(D) if sm_scale is None else sm_scale
+    worst = max_err = 0.0
+    for h in range(NH):
+        q, k, v = head64("q", h), head64("k", h), head64("v", h)
+        ref = oracle.coarse_output(q, k, v, vbs, sm_scale)[:, 0]
+        pools = [oracle.mean_pool(x, vbs)[:, 0] for x in (q, k, v, np.abs(q), np.abs(k), np.abs(v))]
+        for b in range(B):
+            tol = coarse_tolerance(*(p[b] for p in pools), vbs, scale)
+            d = np.abs(oc_gpu[b, h].astype(np.float64) - ref[b])
+            assert np.all(np.isfinite(oc_gpu[b, h])), (label, b, h)
+            ratio = float(np.max(d / np.maximum(tol, 1e-300)))
+            worst, max_err = max(worst, ratio), max(max_err, float(d.max()))
+            assert ratio <= 1.0, (label, b, h, ratio, float(d.max()))
+    print(f"[{label}] o_coarse max |d| {max_err:.3g}, worst |d| / bound {worst:.3g}", flush=True)
+    return worst
+
+
+def combine_check(out_bits, o_fine_bits, o_coarse, gc_bits, gf_bits, label: str) -> None:
+    """Gated combine against the oracle: |out - exact| <= 1/2 ulp_bf16(exact)
+    + 2^-23 (|g_c o_c| + |g_f o_f|) (fp32 product and fma, then bf16 rounding
+    to nearest even)."""
+    of, gc, gf = (oracle.decode_bf16(x) for x in (o_fine_bits, gc_bits, gf_bits))
+    oc = np.asarray(o_coarse, np.float64)
+    exact = oracle.gated_combine(of, oc, gc, gf)
+    oc_rows = np.repeat(np.transpose(oc, (0, 2, 1, 3)), 64, axis=1)
+    err32 = 2.0 ** -23 * (np.abs(gc * oc_rows) + np.abs(gf * of))
+    mag = np.abs(exact) + err32
+    ulp = np.exp2(np.floor(np.log2(np.maximum(mag, 2.0 ** -126))) - 7)
+    got = oracle.decode_bf16(out_bits)
+    d = np.abs(got - exact)
+    ratio = d / (0.5 * ulp + err32)
+    n_eq = int(np.sum(got == oracle.round_to_bf16(exact)))
+    print(f"[{label}] equal to the rounded exact value: {n_eq}/{got.size}; worst |d| / bound "
+          f"{ratio.max():.6f}", flush=True)
+    assert np.all(ratio <= 1.0), label

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.vsa_abi_version() == 2
+    assert lib.vsa_abi_version() == 3
     for s, name in [(0, "VSA_OK"), (1, "VSA_ERR_NULL"), (2, "VSA_ERR_SHAPE"),
                     (3, "VSA_ERR_UNSUPPORTED"), (4, "VSA_ERR_RANGE"), (5, "VSA_ERR_WORKSPACE"),
                     (6, "VSA_ERR_HIP")]:
@@ -114,6 +114,45 @@ def test_fwd_validation():
     # one batch of k must span < 4 GiB: Nkv * 64 * NH * D * 2 = Nkv * 16384 here
     assert call(Nkv=1 << 18, topk=3) == _lib.VSA_ERR_UNSUPPORTED
     assert call(ws=P + 128) == _lib.VSA_ERR_WORKSPACE
+
+
+def test_coarse_and_combine_validation():
+    lib = _lib.load()
+    sel = lib.vsa_select_workspace_bytes(1, 2, 8, 64)
+    need = lib.vsa_coarse_workspace_bytes(1, 2, 8, 64)
+    assert need == sel + 1 * 2 * 8 * 64 * 4          # + pooled v, a multiple of 256
+    assert lib.vsa_coarse_workspace_bytes(1, 2, 0, 64) == 0
+
+    def coarse(**kw):
+        a = dict(q=P, k=P, v=P, vbs=P, B=1, Nc=8, NH=2, D=64, topk=3, idx=P, scale=0.0, oc=P,
+                 ws=P, wsb=need)
+        a.update(kw)
+        return lib.vsa_coarse(a["q"], a["k"], a["v"], a["vbs"], a["B"], a["Nc"], a["NH"], a["D"],
+                              a["topk"], a["idx"], a["scale"], a["oc"], a["ws"], a["wsb"], None)
+
+    assert coarse(v=None) == _lib.VSA_ERR_NULL
+    assert coarse(oc=None) == _lib.VSA_ERR_NULL
+    assert coarse(Nc=0) == _lib.VSA_ERR_SHAPE
+    assert coarse(D=96) == _lib.VSA_ERR_UNSUPPORTED
+    assert coarse(Nc=8193) == _lib.VSA_ERR_UNSUPPORTED
+    assert coarse(topk=0) == _lib.VSA_ERR_RANGE
+    assert coarse(topk=9) == _lib.VSA_ERR_RANGE
+    assert coarse(scale=float("inf")) == _lib.VSA_ERR_RANGE
+    assert coarse(oc=P + 4) == _lib.VSA_ERR_UNSUPPORTED
+    assert coarse(wsb=need - 1) == _lib.VSA_ERR_WORKSPACE
+    assert coarse(ws=P + 64) == _lib.VSA_ERR_WORKSPACE
+
+    def comb(**kw):
+        a = dict(of=P, oc=P, gc=P, gf=P, out=P, B=1, Nc=8, NH=2, D=64)
+        a.update(kw)
+        return lib.vsa_gate_combine(a["of"], a["oc"], a["gc"], a["gf"], a["out"], a["B"], a["Nc"],
+                                    a["NH"], a["D"], None)
+
+    assert comb(gf=None) == _lib.VSA_ERR_NULL
+    assert comb(Nc=-1) == _lib.VSA_ERR_SHAPE
+    assert comb(D=32) == _lib.VSA_ERR_UNSUPPORTED
+    assert comb(out=P + 8) == _lib.VSA_ERR_UNSUPPORTED
+    assert comb(Nc=1 << 26) == _lib.VSA_ERR_SHAPE      # more token rows than grid slots
 
 
 def test_validate_topk_validation():

@@ -11,7 +11,7 @@ import pytest
 import oracle
 from oracle import vsa_oracle as vo
 
-from test_oracle_pins import _dense_masked, _random_topk, _tiled_case
+from test_oracle_pins import _dense_masked, _random_topk, _tiled_case, coarse_sdpa_error
 
 
 def _fwd_no_vbs(q_t, k_t, v_t, topk_idx, vbs, b, h, c, sm_scale=None):
@@ -79,3 +79,44 @@ def test_tile_pin_catches_column_major_cube_order():
     perm = [((cw * Nh + ch) * Nt + ct) for ct in range(Nt) for ch in range(Nh) for cw in range(Nw)]
     bad = good[np.argsort(perm)]
     assert not np.array_equal(bad, good)
+
+
+_orig_coarse = vo.coarse_output
+
+
+def _coarse_all_cubes(q_t, k_t, v_t, vbs, sm_scale=None):
+    # empty cubes kept as keys (their pooled vectors are 0)
+    Qc, Kc, Vc = (vo.mean_pool(x, vbs) for x in (q_t, k_t, v_t))
+    s = Qc @ np.swapaxes(Kc, -1, -2) / math.sqrt(q_t.shape[-1])
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    return (p @ Vc) / p.sum(axis=-1, keepdims=True)
+
+
+def _coarse_scale_1_over_d(q_t, k_t, v_t, vbs, sm_scale=None):
+    return _orig_coarse(q_t, k_t, v_t, vbs, 1.0 / q_t.shape[-1])
+
+
+def _coarse_swapped_kv(q_t, k_t, v_t, vbs, sm_scale=None):
+    return _orig_coarse(q_t, v_t, k_t, vbs, sm_scale)
+
+
+def _coarse_pool_64(q_t, k_t, v_t, vbs, sm_scale=None):
+    scale = np.asarray(vbs, np.float64)[None, :, None, None].repeat(64, axis=1).reshape(1, -1, 1, 1)
+    f = scale / 64.0      # mean over 64 slots of zero-padded cubes
+    return _orig_coarse(q_t * f, k_t * f, v_t * f, vbs, sm_scale)
+
+
+@pytest.mark.parametrize("mutant", [_coarse_all_cubes, _coarse_scale_1_over_d, _coarse_swapped_kv,
+                                    _coarse_pool_64])
+def test_sdpa_pin_catches_coarse_mutations(mutant):
+    assert coarse_sdpa_error(mutant) > 1e-6
+
+
+def test_combine_pin_catches_swapped_gates(monkeypatch):
+    orig = vo.gated_combine
+    monkeypatch.setattr(vo, "gated_combine", lambda of, oc, gc, gf: orig(of, oc, gf, gc))
+    rng = np.random.default_rng(5)
+    of = rng.standard_normal((1, 64, 1, 4))
+    oc = rng.standard_normal((1, 1, 1, 4))
+    one, zero = np.ones_like(of), np.zeros_like(of)
+    assert not np.array_equal(vo.gated_combine(of, oc, zero, one), of)

@@ -499,3 +499,109 @@ def test_cdf_counts_brute_force_definition():
             total = math.fsum(w)
             n = next(n for n in range(1, 13) if math.fsum(w[:n]) >= tau * total - 1e-12 * total)
             assert cnt[r] == n, (tau, r, cnt[r], n)
+
+
+# ------------------------------------------------------ coarse output, combine
+
+def _pool_matrix(vbs):
+    """(Nc, Nc*64) matrix whose row c averages the real slots of cube c: an
+    independent (matrix) form of the mean-pool."""
+    Nc = vbs.size
+    M = np.zeros((Nc, Nc * 64))
+    for c in range(Nc):
+        if vbs[c] > 0:
+            M[c, 64 * c:64 * c + vbs[c]] = 1.0 / vbs[c]
+    return M
+
+
+def coarse_sdpa_error(coarse_fn=None):
+    """Largest |coarse_fn - SDPA| on a ragged case with empty cubes: torch's
+    fp64 scaled_dot_product_attention on means formed by a pooling matrix, the
+    empty cubes masked out as keys."""
+    coarse_fn = coarse_fn or oracle.coarse_output
+    rng = np.random.default_rng(77)
+    vbs = np.array([64, 0, 17, 5, 64, 1, 0, 40, 33], np.int32)
+    B, NH, D = 2, 3, 16
+    S = vbs.size * 64
+    q, k, v = (rng.standard_normal((B, S, NH, D)) for _ in range(3))
+    got = coarse_fn(q, k, v, vbs)
+    M = torch.from_numpy(_pool_matrix(vbs))
+    pool = lambda x: torch.einsum("cs,bshd->bhcd", M, torch.from_numpy(x))
+    mask = torch.from_numpy(vbs > 0)[None, None, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(pool(q), pool(k), pool(v),
+                                                           attn_mask=mask).numpy()
+    return float(np.max(np.abs(got - ref)))
+
+
+def test_coarse_output_equals_sdpa_on_pooled_cubes():
+    """VSA blog, "Two-Stage Architecture": coarse attention over mean-pooled
+    cubes, against an independent formulation (pooling matrix + library SDPA)."""
+    assert coarse_sdpa_error() < 1e-13
+    vbs = np.array([64, 0, 17, 5], np.int32)
+    q, k, v = (_randn(1, 4 * 64, 2, 8) for _ in range(3))
+    # the scale is 1/sqrt(D) by default; an explicit scale is honoured
+    got2 = oracle.coarse_output(q, k, v, vbs, sm_scale=0.3)
+    M = torch.from_numpy(_pool_matrix(vbs))
+    pool = lambda x: torch.einsum("cs,bshd->bhcd", M, torch.from_numpy(x))
+    mask = torch.from_numpy(vbs > 0)[None, None, None, :]
+    ref2 = torch.nn.functional.scaled_dot_product_attention(pool(q), pool(k), pool(v),
+                                                            attn_mask=mask, scale=0.3).numpy()
+    assert np.allclose(got2, ref2, rtol=1e-12, atol=1e-13)
+
+
+def test_coarse_output_closed_forms():
+    """q = 0: every score is 0, so each row is the plain average of the real
+    cubes' mean v. One key cube far ahead of the rest: each row is that cube's
+    mean v. Padding slots never matter."""
+    vbs = np.array([64, 3, 0, 20, 64], np.int32)
+    D = 8
+    S = vbs.size * 64
+    v = _randn(1, S, 1, D)
+    k = _randn(1, S, 1, D)
+    means = np.stack([v[0, 64 * c:64 * c + vbs[c], 0].mean(axis=0) for c in (0, 1, 3, 4)])
+    got = oracle.coarse_output(np.zeros((1, S, 1, D)), k, v, vbs)
+    assert np.allclose(got[0, 0], means.mean(axis=0)[None, :], rtol=0, atol=1e-14)
+
+    u = np.ones(D)
+    q = np.tile(u, (1, S, 1, 1))
+    k = np.zeros((1, S, 1, D))
+    k[0, 64 * 3:64 * 3 + 20, 0] = 40.0 * u            # cube 3 dominates: score 40 D
+    got = oracle.coarse_output(q, k, v, vbs)
+    real = vbs > 0
+    assert np.allclose(got[0, 0][real], means[2][None, :], rtol=0, atol=1e-12)
+    # the empty query cube pools to 0, so its row is again the plain average
+    assert np.allclose(got[0, 0][~real], means.mean(axis=0)[None, :], rtol=0, atol=1e-14)
+
+    poisoned = v.copy()
+    for c in range(vbs.size):
+        poisoned[0, 64 * c + vbs[c]:64 * (c + 1)] = 1e30
+    q = _randn(1, S, 1, D)
+    assert np.array_equal(oracle.coarse_output(q, k, v, vbs), oracle.coarse_output(q, k, poisoned, vbs))
+
+
+def test_coarse_output_no_real_key_cube_is_zero():
+    vbs = np.zeros(3, np.int32)
+    x = _randn(1, 3 * 64, 2, 4)
+    assert np.array_equal(oracle.coarse_output(x, x, x, vbs), np.zeros((1, 2, 3, 4)))
+
+
+def test_gated_combine_brute_force_and_special_gates():
+    """VSA blog, "Two-Stage Architecture": out = g_c * Oc + g_f * O_fine with
+    the coarse row broadcast to its cube's 64 rows; checked element by element,
+    and gates (1, 0) / (0, 1) give the branches themselves."""
+    B, Nc, NH, D = 2, 3, 2, 4
+    S = Nc * 64
+    of, gc, gf = (_randn(B, S, NH, D) for _ in range(3))
+    oc = _randn(B, NH, Nc, D)
+    got = oracle.gated_combine(of, oc, gc, gf)
+    for b in range(B):
+        for s in range(0, S, 7):
+            for h in range(NH):
+                for d in range(D):
+                    want = gc[b, s, h, d] * oc[b, h, s // 64, d] + gf[b, s, h, d] * of[b, s, h, d]
+                    assert got[b, s, h, d] == want
+    one, zero = np.ones_like(of), np.zeros_like(of)
+    assert np.array_equal(oracle.gated_combine(of, oc, zero, one), of)
+    bc = oracle.gated_combine(of, oc, one, zero)
+    for s in range(S):
+        assert np.array_equal(bc[:, s], oc[:, :, s // 64])

@@ -42,6 +42,10 @@ SIGNATURES = {
                          _c_int, ctypes.c_float, _vp, _sz, _vp]),
     "vsa_fwd_lut": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
                              _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _sz, _vp]),
+    "vsa_coarse_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int]),
+    "vsa_coarse": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp,
+                            ctypes.c_float, _vp, _vp, _sz, _vp]),
+    "vsa_gate_combine": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp]),
     "vsa_validate_topk": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
 }
 

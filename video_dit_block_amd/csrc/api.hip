@@ -208,6 +208,67 @@ int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                   "select_cdf");
 }
 
+size_t vsa_coarse_workspace_bytes(int32_t B, int32_t NH, int32_t Nc, int32_t D) {
+  if (B <= 0 || NH <= 0 || Nc <= 0 || D <= 0) return 0;
+  return vsa::coarse_workspace_bytes(B, NH, Nc, D);
+}
+
+int32_t vsa_coarse(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                   const vsa_bf16_t* v_tiled, const int32_t* vbs, int32_t B, int32_t Nc,
+                   int32_t NH, int32_t D, int32_t topk, int32_t* topk_idx, float sm_scale,
+                   float* o_coarse, void* workspace, size_t workspace_bytes,
+                   vsa_stream_t stream) {
+  if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || vbs == nullptr ||
+      o_coarse == nullptr)
+    return fail(VSA_ERR_NULL, "q_tiled, k_tiled, v_tiled, vbs or o_coarse is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  if (Nc <= 0) return fail(VSA_ERR_SHAPE, "Nc=%d must be positive", Nc);
+  if (Nc > VSA_MAX_CUBES)
+    return fail(VSA_ERR_UNSUPPORTED, "Nc=%d exceeds VSA_MAX_CUBES=%d", Nc, VSA_MAX_CUBES);
+  if ((int64_t)B * NH > kMaxGridYZ)
+    return fail(VSA_ERR_SHAPE, "B*NH=%lld exceeds %lld", (long long)B * NH, (long long)kMaxGridYZ);
+  if (topk_idx != nullptr && (topk < 1 || topk > Nc))
+    return fail(VSA_ERR_RANGE, "topk=%d outside [1, %d]", topk, Nc);
+  if (!isfinite(sm_scale)) return fail(VSA_ERR_RANGE, "sm_scale is not finite");
+  if (!aligned16(q_tiled) || !aligned16(k_tiled) || !aligned16(v_tiled) || !aligned16(o_coarse))
+    return fail(VSA_ERR_UNSUPPORTED, "q_tiled, k_tiled, v_tiled and o_coarse must be 16-byte aligned");
+  const size_t need = vsa::coarse_workspace_bytes(B, NH, Nc, D);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(VSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_coarse(q_tiled, k_tiled, v_tiled, vbs, B, Nc, NH, D, topk,
+                                     topk_idx, sm_scale, o_coarse, workspace,
+                                     static_cast<hipStream_t>(stream)),
+                  "coarse");
+}
+
+int32_t vsa_gate_combine(const vsa_bf16_t* o_fine, const float* o_coarse,
+                         const vsa_bf16_t* gate_coarse, const vsa_bf16_t* gate_fine,
+                         vsa_bf16_t* out, int32_t B, int32_t Nc, int32_t NH, int32_t D,
+                         vsa_stream_t stream) {
+  if (o_fine == nullptr || o_coarse == nullptr || gate_coarse == nullptr ||
+      gate_fine == nullptr || out == nullptr)
+    return fail(VSA_ERR_NULL, "o_fine, o_coarse, gate_coarse, gate_fine or out is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  if (Nc <= 0) return fail(VSA_ERR_SHAPE, "Nc=%d must be positive", Nc);
+  if ((int64_t)B * Nc * 64 > kMaxGridX)
+    return fail(VSA_ERR_SHAPE, "B*Nc*64=%lld exceeds %lld", (long long)B * Nc * 64,
+                (long long)kMaxGridX);
+  if (!aligned16(o_fine) || !aligned16(o_coarse) || !aligned16(gate_coarse) ||
+      !aligned16(gate_fine) || !aligned16(out))
+    return fail(VSA_ERR_UNSUPPORTED, "all buffers must be 16-byte aligned");
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_gate_combine(o_fine, o_coarse, gate_coarse, gate_fine, out, B, Nc,
+                                           NH, D, static_cast<hipStream_t>(stream)),
+                  "gate_combine");
+}
+
 size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
                                int32_t topk) {
   if (B <= 0 || Nq <= 0 || Nkv <= 0 || NH <= 0 || D <= 0 || topk <= 0) return 0;

@@ -20,6 +20,32 @@ struct SelectWorkspace {
 };
 SelectWorkspace select_workspace(int B, int NH, int Nc, int D);
 
+// Selector pieces: mean of the real rows of every cube into fp32
+// [B][NH][Nc][D] (launch_pool: one tensor into xc; launch_pool_scores: q and k
+// into the workspace's Qc and Kc, then S = Qc . Kc^T), and the per-row top-k
+// (with the CDF count when valid != nullptr) over S [BH][Nc][Nc].
+hipError_t launch_pool(const uint16_t* x_tiled, const int32_t* vbs, int B, int Nc, int NH,
+                       int D, float* xc, hipStream_t stream);
+hipError_t launch_pool_scores(const uint16_t* q_tiled, const uint16_t* k_tiled,
+                              const int32_t* vbs, int B, int Nc, int NH, int D,
+                              void* workspace, hipStream_t stream);
+hipError_t launch_topk(const float* s, int BH, int Nc, int topk, int32_t* topk_idx,
+                       int32_t* valid, float scale, float tau, hipStream_t stream);
+
+// Coarse stage: its workspace is the selector's (Qc, Kc, S) followed by Vc.
+// Pools q, k and v, scores the cubes, optionally writes the top-k ids
+// (topk_idx != nullptr), and writes O_c = softmax(S scale) V_c over the key
+// cubes holding a real token, fp32 [B][NH][Nc][D].
+size_t coarse_workspace_bytes(int B, int NH, int Nc, int D);
+hipError_t launch_coarse(const uint16_t* q_tiled, const uint16_t* k_tiled,
+                         const uint16_t* v_tiled, const int32_t* vbs, int B, int Nc, int NH,
+                         int D, int topk, int32_t* topk_idx, float scale, float* o_coarse,
+                         void* workspace, hipStream_t stream);
+// out = gate_c * O_c[cube of the row] + gate_f * o_fine, rounded to bf16.
+hipError_t launch_gate_combine(const uint16_t* o_fine, const float* o_coarse,
+                               const uint16_t* gate_c, const uint16_t* gate_f, uint16_t* out,
+                               int B, int Nc, int NH, int D, hipStream_t stream);
+
 // valid != nullptr: also write the CDF count per row (scale, tau).
 hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          const int32_t* vbs, int B, int Nc, int NH, int D,

@@ -233,6 +233,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 
 }  // namespace
 
+hipError_t launch_pool(const uint16_t* x_tiled, const int32_t* vbs, int B, int Nc, int NH,
+                       int D, float* xc, hipStream_t stream) {
+  hipLaunchKernelGGL(pool_kernel, dim3(Nc, B, 1), dim3(kPoolThreads), 0, stream,
+                     reinterpret_cast<const u32x4*>(x_tiled),
+                     reinterpret_cast<const u32x4*>(x_tiled), vbs, xc, xc, Nc, NH, D);
+  return hipGetLastError();
+}
+
 SelectWorkspace select_workspace(int B, int NH, int Nc, int D) {
   SelectWorkspace w;
   const size_t pooled = (size_t)B * NH * Nc * D * sizeof(float);
@@ -243,10 +251,9 @@ SelectWorkspace select_workspace(int B, int NH, int Nc, int D) {
   return w;
 }
 
-hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
-                         const int32_t* vbs, int B, int Nc, int NH, int D,
-                         int topk, int32_t* topk_idx, int32_t* valid, float scale, float tau,
-                         void* workspace, hipStream_t stream) {
+hipError_t launch_pool_scores(const uint16_t* q_tiled, const uint16_t* k_tiled,
+                              const int32_t* vbs, int B, int Nc, int NH, int D,
+                              void* workspace, hipStream_t stream) {
   const SelectWorkspace w = select_workspace(B, NH, Nc, D);
   char* ws = static_cast<char*>(workspace);
   float* qc = reinterpret_cast<float*>(ws + w.qc_off);
@@ -265,16 +272,29 @@ hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
     hipLaunchKernelGGL(score_kernel<128>, sgrid, dim3(kScoreThreads), 0, stream, qc, kc, s, Nc);
   else
     hipLaunchKernelGGL(score_kernel<64>, sgrid, dim3(kScoreThreads), 0, stream, qc, kc, s, Nc);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+hipError_t launch_topk(const float* s, int BH, int Nc, int topk, int32_t* topk_idx,
+                       int32_t* valid, float scale, float tau, hipStream_t stream) {
   int n_pow2 = 1;
   while (n_pow2 < Nc) n_pow2 <<= 1;
   if (n_pow2 < 2) n_pow2 = 2;
-  hipLaunchKernelGGL(topk_kernel, dim3(Nc, B * NH), dim3(kTopkThreads),
+  hipLaunchKernelGGL(topk_kernel, dim3(Nc, BH), dim3(kTopkThreads),
                      (size_t)n_pow2 * sizeof(uint64_t), stream, s, topk_idx, Nc,
                      n_pow2, topk, valid, scale, tau);
   return hipGetLastError();
+}
+
+hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
+                         const int32_t* vbs, int B, int Nc, int NH, int D,
+                         int topk, int32_t* topk_idx, int32_t* valid, float scale, float tau,
+                         void* workspace, hipStream_t stream) {
+  hipError_t e = launch_pool_scores(q_tiled, k_tiled, vbs, B, Nc, NH, D, workspace, stream);
+  if (e != hipSuccess) return e;
+  const float* s = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
+                                                  select_workspace(B, NH, Nc, D).s_off);
+  return launch_topk(s, B * NH, Nc, topk, topk_idx, valid, scale, tau, stream);
 }
 
 }  // namespace vsa

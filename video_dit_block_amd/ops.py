@@ -222,6 +222,64 @@ def fwd_lut(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
     return (out, lse, mp) if stats else out
 
 
+def coarse_workspace_bytes(B: int, NH: int, Nc: int, D: int) -> int:
+    return int(_lib.load().vsa_coarse_workspace_bytes(B, NH, Nc, D))
+
+
+def coarse(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, vbs: torch.Tensor,
+           topk: int | None = None, sm_scale: float | None = None,
+           workspace: torch.Tensor | None = None):
+    """Coarse stage over mean-pooled cubes: o_coarse float32 (B, NH, Nc, D),
+    and with ``topk`` also the selector's ids (B, NH, Nc, topk) from the same
+    scores, returned as (o_coarse, topk_idx)."""
+    for t, n in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
+        _bf16(t, n)
+    _i32(vbs, "vbs")
+    B, S, NH, D = q_t.shape
+    Nc = S // CUBE
+    if k_t.shape != q_t.shape or v_t.shape != q_t.shape or S % CUBE:
+        raise ValueError("q_t, k_t and v_t must all be (B, Nc*64, NH, D)")
+    if workspace is None:
+        workspace = torch.empty(coarse_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8,
+                                device=q_t.device)
+    oc = torch.empty((B, NH, Nc, D), dtype=torch.float32, device=q_t.device)
+    idx = None
+    if topk is not None:
+        idx = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=q_t.device)
+    scale = 0.0 if sm_scale is None else float(sm_scale)
+    _lib.check(_lib.load().vsa_coarse(q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(),
+                                      vbs.data_ptr(), B, Nc, NH, D, 0 if topk is None else topk,
+                                      _ptr(idx), scale, oc.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream()),
+               "vsa_coarse")
+    return oc if topk is None else (oc, idx)
+
+
+def gate_combine(o_fine: torch.Tensor, o_coarse: torch.Tensor, gate_coarse: torch.Tensor,
+                 gate_fine: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = gate_coarse * o_coarse[cube of the row] + gate_fine * o_fine, bf16
+    (B, Nc*64, NH, D); ``out`` may be ``o_fine`` itself."""
+    for t, n in ((o_fine, "o_fine"), (gate_coarse, "gate_coarse"), (gate_fine, "gate_fine")):
+        _bf16(t, n)
+    B, S, NH, D = o_fine.shape
+    Nc = S // CUBE
+    if S % CUBE or gate_coarse.shape != o_fine.shape or gate_fine.shape != o_fine.shape:
+        raise ValueError("o_fine and both gates must be (B, Nc*64, NH, D)")
+    if (o_coarse.dtype != torch.float32 or not o_coarse.is_cuda or not o_coarse.is_contiguous()
+            or tuple(o_coarse.shape) != (B, NH, Nc, D)):
+        raise ValueError(f"o_coarse must be a contiguous float32 CUDA tensor ({B}, {NH}, {Nc}, {D})")
+    if out is None:
+        out = torch.empty_like(o_fine)
+    _bf16(out, "out")
+    if out.shape != o_fine.shape:
+        raise ValueError("out must match o_fine")
+    _lib.check(_lib.load().vsa_gate_combine(o_fine.data_ptr(), o_coarse.data_ptr(),
+                                            gate_coarse.data_ptr(), gate_fine.data_ptr(),
+                                            out.data_ptr(), B, Nc, NH, D, _stream()),
+               "vsa_gate_combine")
+    return out
+
+
 def validate_topk(topk_idx: torch.Tensor, Nkv: int) -> int:
     """Number of out-of-range or repeated ids in topk_idx (B, NH, Nq, topk)."""
     _i32(topk_idx, "topk_idx")
