@@ -10,8 +10,12 @@ events on the stream the library launches on (torch's current stream).
 The headline figure is the fine forward (vsa_fwd): kernel-only, warmed,
 effective TFLOP/s = 4 * D * 64 * sum over (b, h, query cube) of the real
 tokens of the selected cubes, divided by its mean launch time. The same
-kernel is also timed at topk = all (dense). The CPU oracle is timed on a
-bounded sample of the same workload as a reported baseline.
+kernel is also timed at topk = all (dense). Further legs on the same tensors:
+the lookup-table path (cumulative-mass selector + vsa_fwd_lut with its row
+statistics), the two-stage path (coarse output, gated combine), the fine
+kernel in Hilbert cube order, and the block mask -> LUT compaction. The CPU
+oracle is timed on a bounded sample of the same workload as a reported
+baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu]
 """
@@ -389,6 +393,47 @@ def main():
     }
     del wsc, oc, idx2, gc, gf, comb
 
+    # cube order and mask legs: the fine kernel on the same tensors tiled in
+    # 3D Hilbert cube order (selector rerun on them), and the compaction of
+    # the top-k selection written as a dense block mask into the LUT
+    order = vsa.cube_order(T, H, W, "hilbert").to(dev)
+    qh, kh, vh = (torch.empty_like(qt) for _ in range(3))
+    vbs_hil = torch.empty_like(vbs)
+    for src, dst in ((q, qh), (k, kh), (v, vh)):
+        vsa.tile(src, T, H, W, out=dst, vbs=vbs_hil, order=order)
+    idx_hil = vsa.select(qh, kh, vbs_hil, topk, workspace=ws)
+    out_h = torch.empty_like(qt)
+    mask = torch.zeros((B, NH, Nc, Nc), dtype=torch.uint8, device=dev)
+    mask.scatter_(3, idx.long(), 1)
+    lut_ids = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=dev)
+    lut_cnt = torch.empty((B, NH, Nc), dtype=torch.int32, device=dev)
+    for name, fn in (("fwd_hilbert", lambda: vsa.fwd(qh, kh, vh, idx_hil, vbs_hil, out=out_h,
+                                                     workspace=wsf)),
+                     ("mask_to_lut", lambda: lib.vsa_mask_to_lut(mask.data_ptr(), B, NH, Nc, Nc,
+                                                                 topk, lut_ids.data_ptr(),
+                                                                 lut_cnt.data_ptr(), None,
+                                                                 stream))):
+        fn()
+        torch.cuda.synchronize()
+        reps_o = max(reps_d, 10)
+        e0.record()
+        for _ in range(reps_o):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        timed[name] = e0.elapsed_time(e1) / reps_o
+    hfl = fwd_flops(idx_hil.cpu().numpy(), vbs_hil.cpu().numpy(), D)
+    mask_bytes = mask.numel() + lut_ids.numel() * 4 + lut_cnt.numel() * 4
+    order_mask = {
+        "hilbert_fwd_ms": round(timed["fwd_hilbert"], 4),
+        "hilbert_fwd_tflops": round(hfl / timed["fwd_hilbert"] / 1e9, 1),
+        "row_major_fwd_ms": round(fwd_ms, 4),
+        "mask_to_lut_ms": round(timed["mask_to_lut"], 4),
+        "mask_to_lut_gbs": round(mask_bytes / (timed["mask_to_lut"] * 1e-3) / 1e9, 1),
+        "lut_equals_sorted_topk": bool(torch.equal(lut_ids, torch.sort(idx, dim=-1).values)),
+    }
+    del qh, kh, vh, out_h, mask, lut_ids, lut_cnt, idx_hil
+
     # tiling traffic: read real rows, write all rows, per tensor
     tile_bytes = 3 * (T * H * W + S) * NH * D * 2
     cpu = None if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
@@ -432,6 +477,7 @@ def main():
     }
     line["lut"] = lut
     line["two_stage"] = two_stage
+    line["order_mask"] = order_mask
     if sweep is not None:
         line["sweep"] = sweep
     if args.hy720:

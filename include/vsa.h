@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 3
+#define VSA_ABI_VERSION 4
 #define VSA_CUBE 64
 
 typedef uint16_t vsa_bf16_t; /* raw bf16 bits */
@@ -105,6 +105,42 @@ int32_t vsa_tile(const vsa_bf16_t* x, vsa_bf16_t* x_tiled, int32_t* vbs,
 int32_t vsa_untile(const vsa_bf16_t* y_tiled, vsa_bf16_t* y, int32_t B,
                    int32_t T, int32_t H, int32_t W, int32_t NH, int32_t D,
                    vsa_stream_t stream);
+
+/* Cube orders for vsa_tile_ordered (VSA blog, "Two-Stage Architecture",
+ * pre-stage: tokens are reordered along a 3D space-filling curve so that each
+ * attention block covers a compact spatial-temporal region; the curve is not
+ * named). */
+#define VSA_ORDER_ROW_MAJOR 0 /* tiled cube p = row-major cube p (vsa_tile's order) */
+#define VSA_ORDER_HILBERT 1   /* 3D Hilbert curve over the cube grid */
+
+/* Host, pure. Writes order[p] = the row-major id (ct * Nh + ch) * Nw + cw of the
+ * cube placed at tiled position p, for p < vsa_num_cubes(T, H, W), into the
+ * HOST buffer order of n_order entries. VSA_ORDER_HILBERT sorts the cubes by
+ * their index on the 3D Hilbert curve of the smallest power-of-two box that
+ * holds the cube grid (J. Skilling, "Programming the Hilbert curve", AIP Conf.
+ * Proc. 707, 2004: axes-to-transpose transform, bits interleaved with ct
+ * first), so consecutive cubes of a power-of-two grid are face neighbours.
+ * Errors: VSA_ERR_NULL, VSA_ERR_SHAPE (bad grid, n_order too small),
+ * VSA_ERR_RANGE (kind), VSA_ERR_UNSUPPORTED (a grid side above 2^21 cubes). */
+int32_t vsa_cube_order_host(int32_t T, int32_t H, int32_t W, int32_t kind, int32_t* order,
+                            int32_t n_order);
+
+/* vsa_tile with a cube order: tiled cube p holds row-major cube order[p], and
+ * vbs[p] is that cube's real-token count. order is a DEVICE array of
+ * vsa_num_cubes(T, H, W) int32 forming a permutation (a precondition; entries
+ * are clamped into range, so a bad table gives wrong rows but no access out
+ * of bounds). The selector and the fine stage take the result as they take
+ * vsa_tile's. Other arguments and errors as vsa_tile (VSA_ERR_NULL also for a
+ * NULL order). */
+int32_t vsa_tile_ordered(const vsa_bf16_t* x, vsa_bf16_t* x_tiled, int32_t* vbs,
+                         const int32_t* order, int32_t B, int32_t T, int32_t H, int32_t W,
+                         int32_t NH, int32_t D, vsa_stream_t stream);
+
+/* Inverse of vsa_tile_ordered for the same order table. Errors as
+ * vsa_untile (VSA_ERR_NULL also for a NULL order). */
+int32_t vsa_untile_ordered(const vsa_bf16_t* y_tiled, vsa_bf16_t* y, const int32_t* order,
+                           int32_t B, int32_t T, int32_t H, int32_t W, int32_t NH, int32_t D,
+                           vsa_stream_t stream);
 
 /* Bytes of device workspace vsa_select needs: pooled q and k (fp32,
  * [B][NH][Nc][D] each) and the cube score matrix (fp32, [B][NH][Nc][Nc]).
@@ -291,6 +327,24 @@ int32_t vsa_gate_combine(const vsa_bf16_t* o_fine, const float* o_coarse,
                          const vsa_bf16_t* gate_coarse, const vsa_bf16_t* gate_fine,
                          vsa_bf16_t* out, int32_t B, int32_t Nc, int32_t NH, int32_t D,
                          vsa_stream_t stream);
+
+/* Block mask -> lookup table (VSA blog, "Sparse Encoding in CK Tile": Jenga
+ * keeps the full block relation matrix B and skips cells with B[i][j] = 0;
+ * VSA keeps the selected block ids and a valid count per query block). For
+ * every row r = (b, h, i) of block_mask:
+ *   kv_block_idx[r][0 .. n)  = the ids j with block_mask[r][j] != 0, ascending
+ *   valid_block_num[r]       = n = min(number of such j, max_kv)
+ * Entries of kv_block_idx[r] at positions >= n are not written. A row with
+ * more than max_kv set cells keeps its max_kv lowest ids and adds 1 to
+ * *n_truncated (a device int32 the caller zeroes first; may be NULL).
+ *   block_mask       [B][NH][Nq][Nkv] uint8 device array (any nonzero = set)
+ *   kv_block_idx     [B][NH][Nq][max_kv] int32 device output
+ *   valid_block_num  [B][NH][Nq] int32 device output
+ * The output feeds vsa_fwd_lut directly. Errors: VSA_ERR_NULL, VSA_ERR_SHAPE,
+ * VSA_ERR_RANGE (max_kv outside [1, Nkv]), VSA_ERR_HIP. */
+int32_t vsa_mask_to_lut(const uint8_t* block_mask, int32_t B, int32_t NH, int32_t Nq,
+                        int32_t Nkv, int32_t max_kv, int32_t* kv_block_idx,
+                        int32_t* valid_block_num, int32_t* n_truncated, vsa_stream_t stream);
 
 /* Checks the vsa_fwd precondition on topk_idx on the device: counts, into
  * *bad_count (one int32 in device memory, which the caller zeroes first), the

@@ -45,6 +45,12 @@ What it computes, and where the pages define it:
   entries); Wan INT8 blog, "Dynamic Sparsity Budgeting via Softmax
   Normalizer Registers" (max_prob = 1 / l_i).
 
+* ``cube_order`` (with ``tile(..., order)``) and ``mask_to_lut`` -- the
+  space-filling-curve cube order, and the conversion of a block relation
+  matrix into the lookup table.
+  Pages: VSA blog, "Two-Stage Architecture" (pre-stage: 3D space-filling
+  curve reordering) and "Sparse Encoding in CK Tile" (Jenga's full M x M
+  block matrix versus VSA's id list with a valid count).
 * ``coarse_output`` / ``gated_combine`` -- the coarse stage's own output,
   attention among the mean-pooled cubes softmax(Qc Kc^T * sm_scale) Vc per
   (batch, head), and the layer output that mixes it with the fine output
@@ -80,6 +86,10 @@ the design notes of the repository):
     the 64 rows of its cube.
 14. The gates are given tensors of the output's shape, applied elementwise;
     how a model computes them (learned projections) is outside the path.
+15. The space-filling curve orders whole 4x4x4 cubes (each block is then a
+    compact region by construction); the curve is the 3D Hilbert curve of
+    the power-of-two box holding the cube grid, restricted to the grid.
+16. mask_to_lut keeps a row's lowest max_kv ids when more cells are set.
 """
 from __future__ import annotations
 
@@ -96,6 +106,9 @@ __all__ = [
     "slot_tokens",
     "tile",
     "untile",
+    "hilbert_index_3d",
+    "cube_order",
+    "mask_to_lut",
     "mean_pool",
     "cube_scores",
     "topk_select",
@@ -208,26 +221,33 @@ def slot_tokens(T: int, H: int, W: int) -> np.ndarray:
     return out
 
 
-def tile(x_nat: np.ndarray, T: int, H: int, W: int) -> tuple[np.ndarray, np.ndarray]:
+def tile(x_nat: np.ndarray, T: int, H: int, W: int, order=None) -> tuple[np.ndarray, np.ndarray]:
     """Natural order (B, T*H*W, NH, D) -> cube-major (B, Nc*64, NH, D), plus vbs.
 
     Works on any dtype (bf16 bit patterns are copied, not converted); padding
-    slots are zero.
+    slots are zero. With ``order`` (see ``cube_order``) tiled cube p is the
+    row-major cube order[p], and vbs follows the same order.
     """
     x_nat = np.asarray(x_nat)
     B, N, NH, D = x_nat.shape
     assert N == T * H * W, (N, T, H, W)
     src = slot_tokens(T, H, W)
     Nc = src.shape[0]
+    vbs = cube_sizes(T, H, W)
+    if order is not None:
+        order = np.asarray(order)
+        assert np.array_equal(np.sort(order), np.arange(Nc)), "order is not a permutation"
+        src, vbs = src[order], vbs[order]
     out = np.zeros((B, Nc * CUBE, NH, D), dtype=x_nat.dtype)
     flat = src.reshape(-1)
     real = flat >= 0
     out[:, real] = x_nat[:, flat[real]]
-    return out, cube_sizes(T, H, W)
+    return out, vbs
 
 
-def untile(y_t: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
-    """Inverse of ``tile``: cube-major (B, Nc*64, NH, D) -> natural order.
+def untile(y_t: np.ndarray, T: int, H: int, W: int, order=None) -> np.ndarray:
+    """Inverse of ``tile`` (for the same ``order``): cube-major (B, Nc*64, NH, D)
+    -> natural order.
 
     Padding slots are dropped (FastVideo STA guide, "Implementation": the tile
     permutation is inverted to restore the sequential order).
@@ -236,11 +256,70 @@ def untile(y_t: np.ndarray, T: int, H: int, W: int) -> np.ndarray:
     B, S, NH, D = y_t.shape
     src = slot_tokens(T, H, W)
     assert S == src.shape[0] * CUBE
+    if order is not None:
+        src = src[np.asarray(order)]
     out = np.empty((B, T * H * W, NH, D), dtype=y_t.dtype)
     flat = src.reshape(-1)
     real = flat >= 0
     out[:, flat[real]] = y_t[:, real]
     return out
+
+
+def hilbert_index_3d(x0: int, x1: int, x2: int, bits: int) -> int:
+    """Index of the point (x0, x1, x2) (each < 2^bits) on the 3D Hilbert curve.
+
+    J. Skilling, "Programming the Hilbert curve" (AIP Conf. Proc. 707, 2004):
+    the coordinates are turned into the curve's "transposed" index (undo the
+    excess work bit plane by bit plane from the top, Gray-encode, fix the
+    parity), whose bits, read plane by plane from the top with x0 first, form
+    the index.
+    """
+    X = [x0, x1, x2]
+    q = 1 << (bits - 1)
+    while q > 1:
+        low = q - 1
+        for i in range(3):
+            if X[i] & q:
+                X[0] ^= low
+            else:
+                swap = (X[0] ^ X[i]) & low
+                X[0] ^= swap
+                X[i] ^= swap
+        q >>= 1
+    X[1] ^= X[0]
+    X[2] ^= X[1]
+    fix = 0
+    q = 1 << (bits - 1)
+    while q > 1:
+        if X[2] & q:
+            fix ^= q - 1
+        q >>= 1
+    X = [v ^ fix for v in X]
+    h = 0
+    for plane in range(bits - 1, -1, -1):
+        for v in X:
+            h = 2 * h + ((v >> plane) & 1)
+    return h
+
+
+def cube_order(T: int, H: int, W: int, kind: str = "hilbert") -> np.ndarray:
+    """Cube order table, int32 (Nc,): entry p is the row-major cube id
+    (ct*Nh + ch)*Nw + cw placed at tiled position p.
+
+    VSA blog, "Two-Stage Architecture", pre-stage: tokens are reordered along a
+    3D space-filling curve. Reading 15: the 4x4x4 cube is the curve's leaf;
+    "hilbert" sorts the cubes by their index on the Hilbert curve of the
+    smallest power-of-two box holding the cube grid; "row_major" is the
+    identity (reading 1).
+    """
+    Nt, Nh, Nw = cube_grid(T, H, W)
+    n = Nt * Nh * Nw
+    if kind == "row_major":
+        return np.arange(n, dtype=np.int32)
+    assert kind == "hilbert", kind
+    bits = max(1, math.ceil(math.log2(max(Nt, Nh, Nw))))
+    key = [hilbert_index_3d(c // (Nh * Nw), (c // Nw) % Nh, c % Nw, bits) for c in range(n)]
+    return np.argsort(np.asarray(key, dtype=np.int64), kind="stable").astype(np.int32)
 
 
 # ---------------------------------------------------------------- selector
@@ -471,3 +550,29 @@ def gated_combine(o_fine, o_coarse, gate_coarse, gate_fine) -> np.ndarray:
     oc_rows = np.repeat(np.transpose(o_coarse, (0, 2, 1, 3)), CUBE, axis=1)  # (B, Nc*64, NH, D)
     return (np.asarray(gate_coarse, np.float64) * oc_rows
             + np.asarray(gate_fine, np.float64) * np.asarray(o_fine, np.float64))
+
+
+# ------------------------------------------------------------ mask -> LUT
+
+def mask_to_lut(block_mask, max_kv: int):
+    """Block relation matrix -> lookup table.
+
+    VSA blog, "Sparse Encoding in CK Tile": Jenga's B[i][j] (attend when
+    nonzero) versus VSA's list of selected block ids plus a valid count per
+    query block. Per row: the ids j with B[i][j] != 0 in ascending order, the
+    first max_kv of them kept; count = min(#set, max_kv). Returns (ids
+    (..., max_kv) int32 with -1 past the count, counts (...) int32, number of
+    rows with more than max_kv set cells).
+    """
+    m = np.asarray(block_mask) != 0
+    lead = m.shape[:-1]
+    ids = np.full(lead + (max_kv,), -1, dtype=np.int32)
+    cnt = np.zeros(lead, dtype=np.int32)
+    truncated = 0
+    for r in np.ndindex(*lead):
+        on = np.flatnonzero(m[r])
+        truncated += int(on.size > max_kv)
+        keep = on[:max_kv]
+        ids[r][:keep.size] = keep
+        cnt[r] = keep.size
+    return ids, cnt, truncated

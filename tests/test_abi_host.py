@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.vsa_abi_version() == 3
+    assert lib.vsa_abi_version() == 4
     for s, name in [(0, "VSA_OK"), (1, "VSA_ERR_NULL"), (2, "VSA_ERR_SHAPE"),
                     (3, "VSA_ERR_UNSUPPORTED"), (4, "VSA_ERR_RANGE"), (5, "VSA_ERR_WORKSPACE"),
                     (6, "VSA_ERR_HIP")]:
@@ -153,6 +153,42 @@ def test_coarse_and_combine_validation():
     assert comb(D=32) == _lib.VSA_ERR_UNSUPPORTED
     assert comb(out=P + 8) == _lib.VSA_ERR_UNSUPPORTED
     assert comb(Nc=1 << 26) == _lib.VSA_ERR_SHAPE      # more token rows than grid slots
+
+
+@pytest.mark.parametrize("grid", [(21, 30, 52), (30, 48, 80), (5, 6, 7), (1, 1, 1), (17, 3, 90),
+                                  (64, 4, 4)])
+def test_cube_order_host_matches_oracle(grid):
+    import numpy as np
+
+    import oracle
+    lib = _lib.load()
+    n = lib.vsa_num_cubes(*grid)
+    for kind, name in ((_lib.VSA_ORDER_HILBERT, "hilbert"), (_lib.VSA_ORDER_ROW_MAJOR, "row_major")):
+        buf = (ctypes.c_int32 * n)()
+        assert lib.vsa_cube_order_host(*grid, kind, buf, n) == _lib.VSA_OK
+        assert np.array_equal(np.frombuffer(buf, dtype=np.int32), oracle.cube_order(*grid, name))
+
+
+def test_order_and_mask_validation():
+    lib = _lib.load()
+    buf = (ctypes.c_int32 * 8)()
+    assert lib.vsa_cube_order_host(5, 6, 7, 1, None, 8) == _lib.VSA_ERR_NULL
+    assert lib.vsa_cube_order_host(5, 6, 7, 1, buf, 7) == _lib.VSA_ERR_SHAPE
+    assert lib.vsa_cube_order_host(5, 6, 7, 2, buf, 8) == _lib.VSA_ERR_RANGE
+    assert lib.vsa_cube_order_host(0, 6, 7, 1, buf, 8) == _lib.VSA_ERR_SHAPE
+    assert lib.vsa_tile_ordered(P, P, None, None, 1, 5, 6, 7, 2, 64, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_tile_ordered(P, P, None, P, 1, 5, 6, 7, 2, 96, None) == _lib.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_untile_ordered(P, P, None, 1, 5, 6, 7, 2, 64, None) == _lib.VSA_ERR_NULL
+    assert lib.vsa_untile_ordered(P, P + 4, P, 1, 5, 6, 7, 2, 64, None) == _lib.VSA_ERR_UNSUPPORTED
+    m = lambda **kw: lib.vsa_mask_to_lut(*[kw.get(k, d) for k, d in (
+        ("mask", P), ("B", 1), ("NH", 2), ("Nq", 8), ("Nkv", 8), ("max_kv", 8), ("idx", P),
+        ("cnt", P), ("tr", None))], None)
+    assert m(mask=None) == _lib.VSA_ERR_NULL
+    assert m(cnt=None) == _lib.VSA_ERR_NULL
+    assert m(Nq=0) == _lib.VSA_ERR_SHAPE
+    assert m(max_kv=0) == _lib.VSA_ERR_RANGE
+    assert m(max_kv=9) == _lib.VSA_ERR_RANGE
+    assert m(B=65536, NH=65536, Nq=2) == _lib.VSA_ERR_SHAPE
 
 
 def test_validate_topk_validation():

@@ -11,7 +11,8 @@ import pytest
 import oracle
 from oracle import vsa_oracle as vo
 
-from test_oracle_pins import _dense_masked, _random_topk, _tiled_case, coarse_sdpa_error
+from test_oracle_pins import (_dense_masked, _random_topk, _tiled_case, coarse_sdpa_error,
+                              mask_lut_pin)
 
 
 def _fwd_no_vbs(q_t, k_t, v_t, topk_idx, vbs, b, h, c, sm_scale=None):
@@ -120,3 +121,46 @@ def test_combine_pin_catches_swapped_gates(monkeypatch):
     oc = rng.standard_normal((1, 1, 1, 4))
     one, zero = np.ones_like(of), np.zeros_like(of)
     assert not np.array_equal(vo.gated_combine(of, oc, zero, one), of)
+
+
+def test_hilbert_pin_catches_a_missing_gray_encode(monkeypatch):
+    def no_gray(x0, x1, x2, bits):
+        # the same construction without the Gray-encode step
+        X = [x0, x1, x2]
+        q = 1 << (bits - 1)
+        while q > 1:
+            low = q - 1
+            for i in range(3):
+                if X[i] & q:
+                    X[0] ^= low
+                else:
+                    t = (X[0] ^ X[i]) & low
+                    X[0] ^= t
+                    X[i] ^= t
+            q >>= 1
+        h = 0
+        for plane in range(bits - 1, -1, -1):
+            for v in X:
+                h = 2 * h + ((v >> plane) & 1)
+        return h
+
+    cells = [(x, y, z) for x in range(4) for y in range(4) for z in range(4)]
+    path = [cells[i] for i in np.argsort([no_gray(*c, 2) for c in cells])]
+    steps = np.abs(np.diff(np.asarray(path), axis=0)).sum(axis=1)
+    assert not np.all(steps == 1)
+
+
+def test_mask_pin_catches_keeping_the_highest_ids():
+    orig = vo.mask_to_lut
+
+    def keep_highest(block_mask, max_kv):
+        m = np.asarray(block_mask) != 0
+        full, cnt_all, _ = orig(m, m.shape[-1])
+        ids, cnt, tr = orig(m, max_kv)
+        for r in np.ndindex(*m.shape[:-1]):
+            n = cnt_all[r]
+            if n > max_kv:
+                ids[r][:max_kv] = full[r][n - max_kv:n]
+        return ids, cnt, tr
+
+    assert not mask_lut_pin(keep_highest)

@@ -605,3 +605,104 @@ def test_gated_combine_brute_force_and_special_gates():
     bc = oracle.gated_combine(of, oc, one, zero)
     for s in range(S):
         assert np.array_equal(bc[:, s], oc[:, :, s // 64])
+
+
+# --------------------------------------------- cube order (SFC), mask -> LUT
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_hilbert_box_order_is_a_unit_step_hierarchical_path(bits):
+    """Defining properties of the 3D Hilbert curve on a 2^b box: the indices are
+    a permutation of [0, 8^b); the path starts at the origin; consecutive cells
+    are face neighbours; every aligned 2^k sub-box is visited contiguously."""
+    n = 1 << bits
+    cells = [(x, y, z) for x in range(n) for y in range(n) for z in range(n)]
+    idx = [oracle.hilbert_index_3d(*c, bits) for c in cells]
+    assert sorted(idx) == list(range(n ** 3))
+    path = [cells[i] for i in np.argsort(idx)]
+    assert path[0] == (0, 0, 0)
+    steps = np.abs(np.diff(np.asarray(path), axis=0)).sum(axis=1)
+    assert np.all(steps == 1)
+    for k in range(1, bits):
+        blocks = [tuple(v >> k for v in c) for c in path]
+        runs = [b for i, b in enumerate(blocks) if i == 0 or b != blocks[i - 1]]
+        assert len(runs) == len(set(runs)) == (n >> k) ** 3
+
+
+def test_cube_order_restricts_the_box_curve():
+    """On a non-power-of-two grid the order is the box curve's order with the
+    cells outside the grid skipped; a permutation; row_major is the identity."""
+    Nt, Nh, Nw = 6, 8, 13                     # the Wan grid 21x30x52
+    order = oracle.cube_order(21, 30, 52)
+    assert np.array_equal(np.sort(order), np.arange(Nt * Nh * Nw))
+    n = 16
+    box = [(t, h, w) for t in range(n) for h in range(n) for w in range(n)]
+    walk = [box[i] for i in np.argsort([oracle.hilbert_index_3d(*c, 4) for c in box])]
+    inside = [(t * Nh + h) * Nw + w for t, h, w in walk if t < Nt and h < Nh and w < Nw]
+    assert np.array_equal(order, inside)
+    assert np.array_equal(oracle.cube_order(21, 30, 52, "row_major"), np.arange(624))
+    # locality: the mean step between consecutive cubes is close to 1
+    xyz = np.stack([order // (Nh * Nw), (order // Nw) % Nh, order % Nw], axis=1)
+    assert np.abs(np.diff(xyz, axis=0)).sum(axis=1).mean() < 1.1
+
+
+def test_tile_with_order_permutes_whole_cubes_and_roundtrips():
+    rng = np.random.default_rng(3)
+    T, H, W = 9, 5, 6
+    x = rng.integers(0, 65535, size=(2, T * H * W, 2, 4), dtype=np.uint16)
+    order = oracle.cube_order(T, H, W)
+    plain, vbs = oracle.tile(x, T, H, W)
+    xt, vbs_o = oracle.tile(x, T, H, W, order)
+    for p, c in enumerate(order):
+        assert np.array_equal(xt[:, 64 * p:64 * (p + 1)], plain[:, 64 * c:64 * (c + 1)])
+        assert vbs_o[p] == vbs[c]
+    assert np.array_equal(oracle.untile(xt, T, H, W, order), x)
+
+
+def mask_lut_pin(fn=None) -> bool:
+    """Brute force over a random mask with an empty and a full row: each row's
+    ids are its set cells in ascending order and give the mask back; with a
+    cap of 4 the counts, the truncated-row tally and the kept (lowest) ids."""
+    fn = fn or oracle.mask_to_lut
+    rng = np.random.default_rng(11)
+    M = rng.random((2, 3, 7, 19)) < 0.3
+    M[0, 0, 0] = False                           # an empty row
+    M[1, 2, 6] = True                            # a full row
+    ids, cnt, trunc = fn(M, 19)
+    ok = trunc == 0
+    for r in np.ndindex(2, 3, 7):
+        want = [j for j in range(19) if M[r][j]]
+        ok &= bool(cnt[r] == len(want) and list(ids[r][:cnt[r]]) == want)
+        back = np.zeros(19, bool)
+        back[ids[r][:cnt[r]]] = True
+        ok &= bool(np.array_equal(back, M[r]))
+    ids4, cnt4, trunc4 = fn(M, 4)
+    ok &= trunc4 == int((M.sum(axis=-1) > 4).sum())
+    ok &= bool(np.array_equal(cnt4, np.minimum(M.sum(axis=-1), 4)))
+    for r in np.ndindex(2, 3, 7):
+        ok &= list(ids4[r][:cnt4[r]]) == [j for j in range(19) if M[r][j]][:4]
+    return bool(ok)
+
+
+def test_mask_to_lut_brute_force_and_roundtrip():
+    assert mask_lut_pin()
+
+
+def test_mask_lut_drives_fwd_lut_like_the_dense_mask():
+    """A block mask turned into the LUT gives, through fwd_lut, the brute-force
+    dense attention under that block mask (and the real-token mask)."""
+    rng = np.random.default_rng(12)
+    q, kk, v, vbs = _tiled_case(9, 5, 6, NH=2, D=8, B=1, rng=rng)
+    Nc = vbs.size
+    M = rng.random((1, 2, Nc, Nc)) < 0.35
+    M[..., 0] = True                             # every row attends cube 0 (64 real tokens)
+    ids, cnt, _ = oracle.mask_to_lut(M, Nc)
+    out, _, _ = oracle.fwd_lut(q, kk, v, np.maximum(ids, 0), cnt, vbs)
+    S = Nc * 64
+    cube_of, slot_of = np.arange(S) // 64, np.arange(S) % 64
+    scale = 1 / math.sqrt(8)
+    for h in range(2):
+        tok = M[0, h][cube_of][:, cube_of] & (slot_of < vbs[cube_of])[None, :]
+        s = np.where(tok, q[0, :, h] @ kk[0, :, h].T * scale, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        ref = p @ v[0, :, h] / p.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(out[0, :, h], ref, rtol=0, atol=1e-12)

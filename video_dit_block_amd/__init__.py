@@ -3,6 +3,6 @@ selector, fine block-sparse attention, the coarse-stage output and the gated
 combine, in HIP kernels behind the C ABI of include/vsa.h. This package holds
 the kernels' sources (csrc/), the build script and a thin torch/ctypes
 binding."""
-from .ops import (coarse, coarse_workspace_bytes, default_scale, fwd,  # noqa: F401
-                  fwd_lut, fwd_workspace_bytes, gate_combine, num_cubes, select, select_cdf,
-                  select_workspace_bytes, tile, untile, validate_topk, vbs_host)
+from .ops import (coarse, coarse_workspace_bytes, cube_order, default_scale, fwd,  # noqa: F401
+                  fwd_lut, fwd_workspace_bytes, gate_combine, mask_to_lut, num_cubes, select,
+                  select_cdf, select_workspace_bytes, tile, untile, validate_topk, vbs_host)

@@ -19,6 +19,9 @@ VSA_ERR_RANGE = 4
 VSA_ERR_WORKSPACE = 5
 VSA_ERR_HIP = 6
 
+VSA_ORDER_ROW_MAJOR = 0
+VSA_ORDER_HILBERT = 1
+
 _c_int = ctypes.c_int32
 _vp = ctypes.c_void_p
 _sz = ctypes.c_size_t
@@ -32,6 +35,13 @@ SIGNATURES = {
     "vsa_vbs_host": (_c_int, [_c_int, _c_int, _c_int, _vp, _c_int]),
     "vsa_tile": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "vsa_untile": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "vsa_cube_order_host": (_c_int, [_c_int, _c_int, _c_int, _c_int, _vp, _c_int]),
+    "vsa_tile_ordered": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _c_int, _vp]),
+    "vsa_untile_ordered": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _vp]),
+    "vsa_mask_to_lut": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                 _vp]),
     "vsa_select_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int]),
     "vsa_select": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                             _sz, _vp]),

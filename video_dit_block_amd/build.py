@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
 
-SOURCES = ["api.hip", "tile.hip", "select.hip", "fwd.hip", "coarse.hip", "validate.hip"]
+SOURCES = ["api.hip", "tile.hip", "select.hip", "fwd.hip", "coarse.hip", "lut.hip", "validate.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

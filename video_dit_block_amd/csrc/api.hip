@@ -122,7 +122,7 @@ int32_t vsa_tile(const vsa_bf16_t* x, vsa_bf16_t* x_tiled, int32_t* vbs, int32_t
   if (!aligned16(x) || !aligned16(x_tiled))
     return fail(VSA_ERR_UNSUPPORTED, "x and x_tiled must be 16-byte aligned");
   if ((s = check_device()) != VSA_OK) return s;
-  return launched(vsa::launch_tile(x, x_tiled, vbs, B, T, H, W, NH, D,
+  return launched(vsa::launch_tile(x, x_tiled, vbs, nullptr, B, T, H, W, NH, D,
                                    static_cast<hipStream_t>(stream)), "tile");
 }
 
@@ -136,8 +136,77 @@ int32_t vsa_untile(const vsa_bf16_t* y_tiled, vsa_bf16_t* y, int32_t B, int32_t 
   if (!aligned16(y) || !aligned16(y_tiled))
     return fail(VSA_ERR_UNSUPPORTED, "y and y_tiled must be 16-byte aligned");
   if ((s = check_device()) != VSA_OK) return s;
-  return launched(vsa::launch_untile(y_tiled, y, B, T, H, W, NH, D,
+  return launched(vsa::launch_untile(y_tiled, y, nullptr, B, T, H, W, NH, D,
                                      static_cast<hipStream_t>(stream)), "untile");
+}
+
+int32_t vsa_cube_order_host(int32_t T, int32_t H, int32_t W, int32_t kind, int32_t* order,
+                            int32_t n_order) {
+  if (order == nullptr) return fail(VSA_ERR_NULL, "order is NULL");
+  const int64_t nc = num_cubes64(T, H, W);
+  if (nc < 0) return fail(VSA_ERR_SHAPE, "grid %dx%dx%d must be positive", T, H, W);
+  if (nc > n_order)
+    return fail(VSA_ERR_SHAPE, "order holds %d entries, %lld needed", n_order, (long long)nc);
+  if (kind != VSA_ORDER_ROW_MAJOR && kind != VSA_ORDER_HILBERT)
+    return fail(VSA_ERR_RANGE, "unknown cube order kind %d", kind);
+  if (!vsa::cube_order(T, H, W, kind, order))
+    return fail(VSA_ERR_UNSUPPORTED, "grid %dx%dx%d too large for a 63-bit Hilbert index", T, H,
+                W);
+  return ok();
+}
+
+int32_t vsa_tile_ordered(const vsa_bf16_t* x, vsa_bf16_t* x_tiled, int32_t* vbs,
+                         const int32_t* order, int32_t B, int32_t T, int32_t H, int32_t W,
+                         int32_t NH, int32_t D, vsa_stream_t stream) {
+  if (order == nullptr) return fail(VSA_ERR_NULL, "order is NULL");
+  if (x == nullptr || x_tiled == nullptr) return fail(VSA_ERR_NULL, "x or x_tiled is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  int64_t nc;
+  if ((s = check_grid(T, H, W, &nc)) != VSA_OK) return s;
+  if (!aligned16(x) || !aligned16(x_tiled))
+    return fail(VSA_ERR_UNSUPPORTED, "x and x_tiled must be 16-byte aligned");
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_tile(x, x_tiled, vbs, order, B, T, H, W, NH, D,
+                                   static_cast<hipStream_t>(stream)), "tile_ordered");
+}
+
+int32_t vsa_untile_ordered(const vsa_bf16_t* y_tiled, vsa_bf16_t* y, const int32_t* order,
+                           int32_t B, int32_t T, int32_t H, int32_t W, int32_t NH, int32_t D,
+                           vsa_stream_t stream) {
+  if (order == nullptr) return fail(VSA_ERR_NULL, "order is NULL");
+  if (y_tiled == nullptr || y == nullptr) return fail(VSA_ERR_NULL, "y_tiled or y is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  int64_t nc;
+  if ((s = check_grid(T, H, W, &nc)) != VSA_OK) return s;
+  if (!aligned16(y) || !aligned16(y_tiled))
+    return fail(VSA_ERR_UNSUPPORTED, "y and y_tiled must be 16-byte aligned");
+  if ((s = check_device()) != VSA_OK) return s;
+  return launched(vsa::launch_untile(y_tiled, y, order, B, T, H, W, NH, D,
+                                     static_cast<hipStream_t>(stream)), "untile_ordered");
+}
+
+int32_t vsa_mask_to_lut(const uint8_t* block_mask, int32_t B, int32_t NH, int32_t Nq,
+                        int32_t Nkv, int32_t max_kv, int32_t* kv_block_idx,
+                        int32_t* valid_block_num, int32_t* n_truncated, vsa_stream_t stream) {
+  if (block_mask == nullptr || kv_block_idx == nullptr || valid_block_num == nullptr)
+    return fail(VSA_ERR_NULL, "block_mask, kv_block_idx or valid_block_num is NULL");
+  if (B <= 0 || NH <= 0 || Nq <= 0 || Nkv <= 0)
+    return fail(VSA_ERR_SHAPE, "B=%d NH=%d Nq=%d Nkv=%d must be positive", B, NH, Nq, Nkv);
+  if (max_kv < 1 || max_kv > Nkv) return fail(VSA_ERR_RANGE, "max_kv=%d outside [1, %d]", max_kv, Nkv);
+  // four rows per workgroup: at most 4 * (2^31 - 1) rows; the mask (rows *
+  // Nkv bytes) then stays far below 2^63
+  const int64_t bh = (int64_t)B * NH;
+  if (bh > 4 * kMaxGridX / Nq)
+    return fail(VSA_ERR_SHAPE, "B*NH*Nq = %lld*%d rows exceed the grid", (long long)bh, Nq);
+  const int64_t rows = bh * Nq;
+  int32_t s = check_device();
+  if (s != VSA_OK) return s;
+  return launched(vsa::launch_mask_to_lut(block_mask, rows, Nkv, max_kv, kv_block_idx,
+                                          valid_block_num, n_truncated,
+                                          static_cast<hipStream_t>(stream)),
+                  "mask_to_lut");
 }
 
 size_t vsa_select_workspace_bytes(int32_t B, int32_t NH, int32_t Nc, int32_t D) {

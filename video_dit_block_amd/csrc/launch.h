@@ -9,10 +9,21 @@
 
 namespace vsa {
 
-hipError_t launch_tile(const uint16_t* x, uint16_t* x_tiled, int32_t* vbs, int B,
-                       int T, int H, int W, int NH, int D, hipStream_t stream);
-hipError_t launch_untile(const uint16_t* y_tiled, uint16_t* y, int B, int T,
-                         int H, int W, int NH, int D, hipStream_t stream);
+// order == nullptr: row-major cube order; else tiled cube p is row-major
+// cube order[p].
+hipError_t launch_tile(const uint16_t* x, uint16_t* x_tiled, int32_t* vbs,
+                       const int32_t* order, int B, int T, int H, int W, int NH, int D,
+                       hipStream_t stream);
+hipError_t launch_untile(const uint16_t* y_tiled, uint16_t* y, const int32_t* order, int B,
+                         int T, int H, int W, int NH, int D, hipStream_t stream);
+// Host: the cube order table (kind 0 row-major, 1 Hilbert); false if the
+// grid is too large for a 63-bit Hilbert index.
+bool cube_order(int T, int H, int W, int kind, int32_t* order);
+// Block mask [rows][Nkv] (nonzero = attend) -> ascending ids per row, count
+// per row (capped at max_kv); rows over the cap add 1 to *n_truncated.
+hipError_t launch_mask_to_lut(const uint8_t* mask, int64_t rows, int Nkv, int max_kv,
+                              int32_t* kv_block_idx, int32_t* valid_block_num,
+                              int32_t* n_truncated, hipStream_t stream);
 
 // Workspace carve-up of vsa_select: pooled q, pooled k, scores.
 struct SelectWorkspace {

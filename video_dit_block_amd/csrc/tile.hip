@@ -12,6 +12,23 @@
 // with 16-byte accesses across its 64 lanes, so every access instruction
 // covers 1 KiB of contiguous memory. Padding slots are written as zeros and
 // never read. The work is a pure copy and is bound by HBM bandwidth.
+//
+// Cube order. By default tiled cube p is the cube with row-major id p,
+// (ct * Nh + ch) * Nw + cw. An order table may instead place row-major cube
+// order[p] at position p; cube_order() builds the row-major table or a 3D
+// Hilbert curve over the cube grid. (The VSA blog, "Two-Stage Architecture",
+// pre-stage: tokens are reordered along a 3D space-filling curve so that each
+// block is a compact spatial-temporal region; the curve is not named. Here
+// the 4x4x4 cube is the curve's leaf, so every block is compact by
+// construction, and the curve orders the cubes.) The Hilbert index of (ct, ch, cw) follows J. Skilling, "Programming
+// the Hilbert curve" (AIP Conf. Proc. 707, 2004): the axes-to-transpose
+// transform, then the bits of the transposed coordinates interleaved, ct
+// first, most significant bit first; cubes are sorted by that index inside
+// the power-of-two box that holds the grid.
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 #include "device.h"
 #include "launch.h"
 
@@ -44,13 +61,17 @@ __device__ __forceinline__ void copy_row(const u32x4* __restrict__ src,
 }
 
 // grid (Nc * kSplit, B), block kThreads. kInverse = false: natural -> tiled;
-// true: tiled -> natural (padding slots skipped).
+// true: tiled -> natural (padding slots skipped). order == nullptr: tiled
+// position p holds row-major cube p; otherwise order[p] (clamped into range,
+// so a bad table gives wrong rows but never an access out of bounds).
 template <bool kInverse>
 __global__ __launch_bounds__(kThreads) void tile_kernel(
     const u32x4* __restrict__ src, u32x4* __restrict__ dst, int32_t* vbs_out,
-    int T, int H, int W, int Nh, int Nw, int cpr) {
-  const int c = blockIdx.x / kSplit;
-  const int part = blockIdx.x - c * kSplit;
+    const int32_t* __restrict__ order, int T, int H, int W, int Nh, int Nw, int cpr) {
+  const int pos = blockIdx.x / kSplit;
+  const int part = blockIdx.x - pos * kSplit;
+  const int n_cubes = gridDim.x / kSplit;
+  const int c = order == nullptr ? pos : min(max(order[pos], 0), n_cubes - 1);
   const int b = blockIdx.y;
   const int cw = c % Nw;
   const int ch = (c / Nw) % Nh;
@@ -58,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
   const int eh = cube_extent(H, ch), ew = cube_extent(W, cw);
   const int n_real = cube_extent(T, ct) * eh * ew;
   if (!kInverse && vbs_out != nullptr && part == 0 && b == 0 && threadIdx.x == 0)
-    vbs_out[c] = n_real;
+    vbs_out[pos] = n_real;
 
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const size_t n_nat = (size_t)T * H * W;
@@ -66,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
 #pragma unroll 1
   for (int r = 0; r < kSlotsPerBlock / 4; ++r) {
     const int u = part * kSlotsPerBlock + r * 4 + wave;
-    const size_t tiled_row = (size_t)b * n_tiled + (size_t)c * kCube + u;
+    const size_t tiled_row = (size_t)b * n_tiled + (size_t)pos * kCube + u;
     if (u < n_real) {
       const size_t nat_row =
           (size_t)b * n_nat + slot_token(u, ct, ch, cw, eh, ew, H, W);
@@ -80,27 +101,76 @@ __global__ __launch_bounds__(kThreads) void tile_kernel(
   }
 }
 
+// Hilbert index of X[0..2] (each < 2^bits, bits <= 21): axes to transpose,
+// then interleave.
+uint64_t hilbert3(uint32_t x0, uint32_t x1, uint32_t x2, int bits) {
+  uint32_t X[3] = {x0, x1, x2};
+  const uint32_t top = 1u << (bits - 1);
+  for (uint32_t q = top; q > 1; q >>= 1) {  // undo excess work
+    const uint32_t p = q - 1;
+    for (int i = 0; i < 3; ++i) {
+      if (X[i] & q) {
+        X[0] ^= p;  // invert the low bits of X[0]
+      } else {
+        const uint32_t t = (X[0] ^ X[i]) & p;  // exchange low bits of X[0], X[i]
+        X[0] ^= t;
+        X[i] ^= t;
+      }
+    }
+  }
+  for (int i = 1; i < 3; ++i) X[i] ^= X[i - 1];  // Gray encode
+  uint32_t t = 0;
+  for (uint32_t q = top; q > 1; q >>= 1)
+    if (X[2] & q) t ^= q - 1;
+  for (int i = 0; i < 3; ++i) X[i] ^= t;
+  uint64_t h = 0;
+  for (int bit = bits - 1; bit >= 0; --bit)
+    for (int i = 0; i < 3; ++i) h = (h << 1) | ((X[i] >> bit) & 1u);
+  return h;
+}
+
 }  // namespace
 
-hipError_t launch_tile(const uint16_t* x, uint16_t* x_tiled, int32_t* vbs, int B,
-                       int T, int H, int W, int NH, int D, hipStream_t stream) {
+bool cube_order(int T, int H, int W, int kind, int32_t* order) {
+  const int Nt = (T + 3) / 4, Nh = (H + 3) / 4, Nw = (W + 3) / 4;
+  const int64_t nc = (int64_t)Nt * Nh * Nw;
+  if (kind == 0) {
+    for (int64_t c = 0; c < nc; ++c) order[c] = (int32_t)c;
+    return true;
+  }
+  int bits = 1;
+  while ((1 << bits) < std::max(Nt, std::max(Nh, Nw))) ++bits;
+  if (bits > 21) return false;
+  std::vector<std::pair<uint64_t, int32_t>> keyed((size_t)nc);
+  for (int64_t c = 0; c < nc; ++c) {
+    const int cw = (int)(c % Nw), ch = (int)((c / Nw) % Nh), ct = (int)(c / ((int64_t)Nw * Nh));
+    keyed[(size_t)c] = {hilbert3((uint32_t)ct, (uint32_t)ch, (uint32_t)cw, bits), (int32_t)c};
+  }
+  std::sort(keyed.begin(), keyed.end());
+  for (int64_t c = 0; c < nc; ++c) order[c] = keyed[(size_t)c].second;
+  return true;
+}
+
+hipError_t launch_tile(const uint16_t* x, uint16_t* x_tiled, int32_t* vbs,
+                       const int32_t* order, int B, int T, int H, int W, int NH, int D,
+                       hipStream_t stream) {
   const int Nt = (T + 3) / 4, Nh = (H + 3) / 4, Nw = (W + 3) / 4;
   const int cpr = NH * D * 2 / 16;
   dim3 grid(Nt * Nh * Nw * kSplit, B);
   hipLaunchKernelGGL(tile_kernel<false>, grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const u32x4*>(x),
-                     reinterpret_cast<u32x4*>(x_tiled), vbs, T, H, W, Nh, Nw, cpr);
+                     reinterpret_cast<u32x4*>(x_tiled), vbs, order, T, H, W, Nh, Nw, cpr);
   return hipGetLastError();
 }
 
-hipError_t launch_untile(const uint16_t* y_tiled, uint16_t* y, int B, int T,
-                         int H, int W, int NH, int D, hipStream_t stream) {
+hipError_t launch_untile(const uint16_t* y_tiled, uint16_t* y, const int32_t* order, int B,
+                         int T, int H, int W, int NH, int D, hipStream_t stream) {
   const int Nt = (T + 3) / 4, Nh = (H + 3) / 4, Nw = (W + 3) / 4;
   const int cpr = NH * D * 2 / 16;
   dim3 grid(Nt * Nh * Nw * kSplit, B);
   hipLaunchKernelGGL(tile_kernel<true>, grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const u32x4*>(y_tiled),
-                     reinterpret_cast<u32x4*>(y), nullptr, T, H, W, Nh, Nw, cpr);
+                     reinterpret_cast<u32x4*>(y), nullptr, order, T, H, W, Nh, Nw, cpr);
   return hipGetLastError();
 }
 

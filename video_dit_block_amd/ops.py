@@ -50,9 +50,32 @@ def vbs_host(T: int, H: int, W: int) -> torch.Tensor:
     return out
 
 
+def cube_order(T: int, H: int, W: int, kind: str = "hilbert") -> torch.Tensor:
+    """Cube order table (int32 CPU tensor (Nc,)): entry p is the row-major id of
+    the cube placed at tiled position p. kind: "row_major" or "hilbert"."""
+    kinds = {"row_major": _lib.VSA_ORDER_ROW_MAJOR, "hilbert": _lib.VSA_ORDER_HILBERT}
+    if kind not in kinds:
+        raise ValueError(f"kind must be one of {sorted(kinds)}")
+    n = num_cubes(T, H, W)
+    out = torch.empty(n, dtype=torch.int32)
+    _lib.check(_lib.load().vsa_cube_order_host(T, H, W, kinds[kind], out.data_ptr(), n),
+               "vsa_cube_order_host")
+    return out
+
+
+def _order(order: torch.Tensor | None, nc: int) -> None:
+    if order is not None:
+        _i32(order, "order")
+        if order.numel() != nc:
+            raise ValueError(f"order must hold Nc = {nc} entries")
+
+
 def tile(x: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = None,
-         vbs: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
-    """(B, T*H*W, NH, D) natural order -> ((B, Nc*64, NH, D) tiled, vbs int32 (Nc,))."""
+         vbs: torch.Tensor | None = None,
+         order: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """(B, T*H*W, NH, D) natural order -> ((B, Nc*64, NH, D) tiled, vbs int32 (Nc,)).
+    ``order`` (device int32 (Nc,), from ``cube_order``) places row-major cube
+    order[p] at tiled position p."""
     _bf16(x, "x")
     B, N, NH, D = x.shape
     if N != T * H * W:
@@ -64,13 +87,21 @@ def tile(x: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = Non
     if vbs is None:
         vbs = torch.empty(nc, dtype=torch.int32, device=x.device)
     _i32(vbs, "vbs")
-    _lib.check(_lib.load().vsa_tile(x.data_ptr(), out.data_ptr(), vbs.data_ptr(), B, T, H, W,
-                                    NH, D, _stream()), "vsa_tile")
+    _order(order, nc)
+    if order is None:
+        _lib.check(_lib.load().vsa_tile(x.data_ptr(), out.data_ptr(), vbs.data_ptr(), B, T, H, W,
+                                        NH, D, _stream()), "vsa_tile")
+    else:
+        _lib.check(_lib.load().vsa_tile_ordered(x.data_ptr(), out.data_ptr(), vbs.data_ptr(),
+                                                order.data_ptr(), B, T, H, W, NH, D, _stream()),
+                   "vsa_tile_ordered")
     return out, vbs
 
 
-def untile(y: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """(B, Nc*64, NH, D) tiled -> (B, T*H*W, NH, D) natural order."""
+def untile(y: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = None,
+           order: torch.Tensor | None = None) -> torch.Tensor:
+    """(B, Nc*64, NH, D) tiled -> (B, T*H*W, NH, D) natural order (``order``: the
+    table the tensor was tiled with)."""
     _bf16(y, "y")
     B, S, NH, D = y.shape
     if S != num_cubes(T, H, W) * CUBE:
@@ -78,8 +109,14 @@ def untile(y: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = N
     if out is None:
         out = torch.empty((B, T * H * W, NH, D), dtype=torch.bfloat16, device=y.device)
     _bf16(out, "out")
-    _lib.check(_lib.load().vsa_untile(y.data_ptr(), out.data_ptr(), B, T, H, W, NH, D,
-                                      _stream()), "vsa_untile")
+    _order(order, S // CUBE)
+    if order is None:
+        _lib.check(_lib.load().vsa_untile(y.data_ptr(), out.data_ptr(), B, T, H, W, NH, D,
+                                          _stream()), "vsa_untile")
+    else:
+        _lib.check(_lib.load().vsa_untile_ordered(y.data_ptr(), out.data_ptr(), order.data_ptr(),
+                                                  B, T, H, W, NH, D, _stream()),
+                   "vsa_untile_ordered")
     return out
 
 
@@ -278,6 +315,28 @@ def gate_combine(o_fine: torch.Tensor, o_coarse: torch.Tensor, gate_coarse: torc
                                             out.data_ptr(), B, Nc, NH, D, _stream()),
                "vsa_gate_combine")
     return out
+
+
+def mask_to_lut(block_mask: torch.Tensor, max_kv: int | None = None,
+                count_truncated: bool = False):
+    """Block mask (B, NH, Nq, Nkv) bool/uint8 -> (kv_block_idx int32 (B, NH, Nq,
+    max_kv), valid_block_num int32 (B, NH, Nq)), ids ascending; with
+    ``count_truncated`` also the number of rows with more than max_kv set cells.
+    Entries past a row's count are left as allocated (zero here)."""
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous()
+            or block_mask.dim() != 4):
+        raise ValueError("block_mask must be a contiguous 4-d bool/uint8 CUDA tensor")
+    B, NH, Nq, Nkv = block_mask.shape
+    max_kv = Nkv if max_kv is None else int(max_kv)
+    idx = torch.zeros((B, NH, Nq, max_kv), dtype=torch.int32, device=block_mask.device)
+    cnt = torch.empty((B, NH, Nq), dtype=torch.int32, device=block_mask.device)
+    trunc = torch.zeros(1, dtype=torch.int32, device=block_mask.device) if count_truncated else None
+    _lib.check(_lib.load().vsa_mask_to_lut(block_mask.data_ptr(), B, NH, Nq, Nkv, max_kv,
+                                           idx.data_ptr(), cnt.data_ptr(), _ptr(trunc), _stream()),
+               "vsa_mask_to_lut")
+    return (idx, cnt, int(trunc.item())) if count_truncated else (idx, cnt)
 
 
 def validate_topk(topk_idx: torch.Tensor, Nkv: int) -> int:
