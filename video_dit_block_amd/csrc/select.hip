@@ -17,11 +17,20 @@
 //                 S = Qc . Kc^T per workgroup. fp32 inputs keep the ranking
 //                 accurate to fp32 rounding (bf16 inputs would perturb scores
 //                 by ~2^-9 relative and reorder near-ties).
-//   topk_kernel   one workgroup per score row: a bitonic sort of 64-bit keys
-//                 (order-preserving score bits, then the complemented cube id)
-//                 in LDS, descending; the first topk ids are written out.
-//                 Equal scores therefore come out by ascending cube id.
-//                 With a CDF threshold tau it also writes the row's count: the
+//   topk_wave_kernel (Nc <= 2048) one wave per score row, rows independent:
+//                 the row's order-preserving score keys sit in registers; a
+//                 4-pass 8-bit radix select (LDS histogram per pass, a wave
+//                 suffix scan to find the digit) finds the k-th largest key;
+//                 the keys above it and the lowest-id keys equal to it are
+//                 compacted with ballots, and only those k are sorted (LDS
+//                 bitonic sort of 64-bit keys: score bits, then the
+//                 complemented cube id), descending.
+//   topk_kernel   (larger rows) one workgroup per score row: a bitonic sort of
+//                 all of the row's 64-bit keys in LDS, descending; the first
+//                 topk ids are written out.
+//                 Both give equal scores by ascending cube id, so their outputs
+//                 are identical.
+//                 With a CDF threshold tau either also writes the row's count: the
 //                 fewest leading cubes whose softmax mass (softmax over all Nc
 //                 scores times `scale`) reaches tau, capped at topk (Wan INT8
 //                 blog, same section: sort block scores per query block and
@@ -231,6 +240,158 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   if (tid == 0) valid[row] = first == 0x7FFFFFFF ? min(Nc, topk) : min(first + 1, topk);
 }
 
+// ---------------------------------------------------------------- top-k, one wave per row
+
+constexpr int kWaveRowsMax = 4;  // rows (waves) per workgroup
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// grid (ceil(rows / waves)), block 64 * waves; dynamic LDS per wave: 256 u32
+// histogram bins + n2 u64 candidate keys (n2 = power of two >= topk). Each
+// wave owns its LDS and its row; no workgroup barrier. Lane l holds the keys
+// of cubes j = 64 i + l, i < KPL (Nc <= 64 KPL).
+template <int KPL>
+__global__ __launch_bounds__(64 * kWaveRowsMax) void topk_wave_kernel(
+    const float* __restrict__ s, int32_t* __restrict__ topk_idx, int64_t rows, int Nc, int n2,
+    int topk, int32_t* __restrict__ valid, float scale, float tau) {
+  extern __shared__ uint32_t smem[];
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + wave;
+  if (row >= rows) return;
+  uint32_t* bins = smem + (size_t)wave * (256 + 2 * n2);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(bins + 256);
+  const float* __restrict__ srow = s + row * Nc;
+  const uint64_t below = (1ull << lane) - 1ull;
+
+  uint32_t key[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int j = 64 * i + lane;
+    key[i] = j < Nc ? order_key(srow[j]) : 0u;
+  }
+
+  // Radix select: after pass p the top 8(p+1) bits of the k-th largest key
+  // are known; krem counts how many keys sharing that prefix still belong to
+  // the top k.
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t krem = (uint32_t)topk;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int b = lane; b < 256; b += 64) bins[b] = 0u;
+    wave_lds_fence();
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (64 * i + lane < Nc && (key[i] & pmask) == prefix)
+        atomicAdd(&bins[(key[i] >> shift) & 255u], 1u);
+    wave_lds_fence();
+    // lane l holds digits 4l .. 4l+3; suf = keys with digit >= 4l
+    const uint32_t b0 = bins[4 * lane], b1 = bins[4 * lane + 1], b2 = bins[4 * lane + 2],
+                   b3 = bins[4 * lane + 3];
+    const uint32_t t = b0 + b1 + b2 + b3;
+    uint32_t suf = t;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_down(suf, off, 64);
+      if (lane + off < 64) suf += o;
+    }
+    // the digit d is the largest with (keys with digit >= d) >= krem; its lane
+    // is the one lane with suf >= krem > suf - t
+    const uint64_t hit = __ballot(suf >= krem && suf - t < krem);
+    const int L = __ffsll((unsigned long long)hit) - 1;
+    uint32_t d = 0, above = 0;  // above = keys with digit > d
+    if (lane == L) {
+      const uint32_t c4 = suf - t, c3 = c4 + b3, c2 = c3 + b2, c1 = c2 + b1;
+      if (c3 >= krem) {
+        d = 4 * L + 3; above = c4;
+      } else if (c2 >= krem) {
+        d = 4 * L + 2; above = c3;
+      } else if (c1 >= krem) {
+        d = 4 * L + 1; above = c2;
+      } else {
+        d = 4 * L; above = c1;
+      }
+    }
+    d = __shfl(d, L, 64);
+    above = __shfl(above, L, 64);
+    krem -= above;
+    prefix |= d << shift;
+    pmask |= 0xFFu << shift;
+  }
+
+  // Compact the top k: keys above the threshold, then the krem lowest-id keys
+  // equal to it (ids ascend with (i, lane)).
+  const int n_gt = topk - (int)krem;
+  int seen_gt = 0, seen_eq = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int j = 64 * i + lane;
+    const bool ok = j < Nc;
+    const bool gt = ok && key[i] > prefix, eq = ok && key[i] == prefix;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    const uint64_t k64 = ((uint64_t)key[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+    if (gt) cand[seen_gt + __popcll(bg & below)] = k64;
+    const int r = seen_eq + __popcll(be & below);
+    if (eq && r < (int)krem) cand[n_gt + r] = k64;
+    seen_gt += __popcll(bg);
+    seen_eq += __popcll(be);
+  }
+  for (int t = topk + lane; t < n2; t += 64) cand[t] = 0ull;
+
+  // Bitonic sort of the n2 candidates, descending (one wave: its LDS accesses
+  // complete in order, the fence keeps the compiler from moving them).
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+      wave_lds_fence();
+      for (int t = lane; t < n2 / 2; t += 64) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const uint64_t a = cand[lo], b = cand[hi];
+        const bool desc = (lo & size) == 0;
+        if (desc ? (a < b) : (a > b)) {
+          cand[lo] = b;
+          cand[hi] = a;
+        }
+      }
+    }
+  }
+  wave_lds_fence();
+  int32_t* __restrict__ out = topk_idx + row * topk;
+  for (int t = lane; t < topk; t += 64)
+    out[t] = (int32_t)(0xFFFFFFFFu - (uint32_t)(cand[t] & 0xFFFFFFFFull));
+  if (valid == nullptr) return;
+
+  // CDF count: w_i = exp((s_i - s_0) scale) with s_0 the row maximum, Z the
+  // sum over all Nc cubes; the count is the smallest n with w_0 + .. + w_{n-1}
+  // >= tau Z over the sorted ids, at most topk.
+  const float s0 = key_score((uint32_t)(cand[0] >> 32));
+  float z = 0.0f;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i)
+    if (64 * i + lane < Nc) z += __expf((key_score(key[i]) - s0) * scale);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+  const float thr = tau * z;
+  float run = 0.0f;
+  int first = -1;
+  for (int t0 = 0; t0 < topk && first < 0; t0 += 64) {
+    const int t = t0 + lane;
+    float sc = t < topk ? __expf((key_score((uint32_t)(cand[t] >> 32)) - s0) * scale) : 0.0f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(sc, off, 64);
+      if (lane >= off) sc += o;
+    }
+    const uint64_t reached = __ballot(t < topk && run + sc >= thr);
+    if (reached != 0ull) first = t0 + __ffsll((unsigned long long)reached) - 1;
+    run += __shfl(sc, 63, 64);
+  }
+  if (lane == 0) valid[row] = first < 0 ? topk : first + 1;
+}
+
 }  // namespace
 
 hipError_t launch_pool(const uint16_t* x_tiled, const int32_t* vbs, int B, int Nc, int NH,
@@ -277,6 +438,25 @@ hipError_t launch_pool_scores(const uint16_t* q_tiled, const uint16_t* k_tiled,
 
 hipError_t launch_topk(const float* s, int BH, int Nc, int topk, int32_t* topk_idx,
                        int32_t* valid, float scale, float tau, hipStream_t stream) {
+  if (Nc <= 64 * 32) {
+    int n2 = 64;
+    while (n2 < topk) n2 <<= 1;
+    const int waves = n2 <= 1024 ? kWaveRowsMax : 2;
+    const int64_t rows = (int64_t)BH * Nc;
+    const dim3 grid((unsigned)((rows + waves - 1) / waves)), block(64 * waves);
+    const size_t lds = (size_t)waves * (256 + 2 * n2) * sizeof(uint32_t);
+#define VSA_TOPK_WAVE(K)                                                                      \
+  hipLaunchKernelGGL(topk_wave_kernel<K>, grid, block, lds, stream, s, topk_idx, rows, Nc, n2, \
+                     topk, valid, scale, tau)
+    if (Nc <= 64) VSA_TOPK_WAVE(1);
+    else if (Nc <= 128) VSA_TOPK_WAVE(2);
+    else if (Nc <= 256) VSA_TOPK_WAVE(4);
+    else if (Nc <= 512) VSA_TOPK_WAVE(8);
+    else if (Nc <= 1024) VSA_TOPK_WAVE(16);
+    else VSA_TOPK_WAVE(32);
+#undef VSA_TOPK_WAVE
+    return hipGetLastError();
+  }
   int n_pow2 = 1;
   while (n_pow2 < Nc) n_pow2 <<= 1;
   if (n_pow2 < 2) n_pow2 = 2;
