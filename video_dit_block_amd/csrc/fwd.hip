@@ -25,11 +25,10 @@
 //   (2 waves per SIMD; 32 KiB of LDS each). Units are numbered head-major and
 //   remapped so each XCD walks a contiguous range. With per-row counts (a
 //   lookup table) a third pre-pass orders each head's query cubes by
-//   descending half-tile count, and that order is the dispatch order inside
-//   the head: with mixed lengths in flight, the short units race ahead through
+//   descending count, and that order is the dispatch order inside the head: with mixed lengths in flight, the short units race ahead through
 //   the key cubes and the L2 reuse between neighbours is lost (measured on
-//   the Wan tensors at a 0.9 mass threshold: 17.0 -> 14.3 ms in a head-major
-//   emulation).
+//   the Wan tensors at a 0.9 mass threshold: 18.5 -> 14.1 ms). Equal counts
+//   keep the plain order, which is the better one then.
 // * K and V half-tiles stream through LDS, each double-buffered, loaded
 //   global -> LDS directly (buffer_load ... lds, two 1 KiB loads per M0
 //   write); every wave loads half of each tile. The buffer range of a load
@@ -296,18 +295,21 @@ __global__ __launch_bounds__(64) void halves_kernel(
 }
 
 // Dispatch order of a lookup table with per-row counts: per (b, h), the query
-// cubes by descending half-tile count (ties by cube id). Units of one head
-// that run side by side then carry similar amounts of work, so they sweep the
-// key cubes at similar rates (their accesses stay close together in L2), and
-// the longest units start first. grid (B*NH), dynamic LDS Nq int32.
+// cubes by descending count of selected cubes (ties by cube id, so equal
+// counts keep the spatial order). Units of one head that run side by side
+// then carry similar amounts of work, so they sweep the key cubes at similar
+// rates (their accesses stay close together in L2), and the longest units
+// start first. grid (B*NH), dynamic LDS Nq int32.
 constexpr int kOrderThreads = 256;
 constexpr int kOrderMaxNq = 4096;
 
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ counts,
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ valid,
+                                                              int row_len,
                                                               int32_t* __restrict__ order, int Nq) {
   extern __shared__ int32_t cnt[];
   const size_t base = (size_t)blockIdx.x * Nq;
-  for (int i = threadIdx.x; i < Nq; i += kOrderThreads) cnt[i] = counts[base + i];
+  for (int i = threadIdx.x; i < Nq; i += kOrderThreads)
+    cnt[i] = min(max(valid[base + i], 0), row_len);
   __syncthreads();
   for (int i = threadIdx.x; i < Nq; i += kOrderThreads) {
     const int ci = cnt[i];
@@ -672,28 +674,29 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      cpr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // The order pass runs ahead of the list pass: launched right before the
+  // fine kernel it cost that kernel about 1 ms at 312 cubes per row
+  // (measured, cause not established).
+  if (valid != nullptr && Nq <= kOrderMaxNq) {
+    order = reinterpret_cast<int32_t*>(ws + w.order_off);
+    hipLaunchKernelGGL(order_kernel, dim3(B * NH), dim3(kOrderThreads), (size_t)Nq * 4, stream,
+                       valid, topk, order, Nq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(halves_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, valid, vbs,
                      list, counts, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (valid != nullptr && Nq <= kOrderMaxNq) {
-    order = reinterpret_cast<int32_t*>(ws + w.order_off);
-    hipLaunchKernelGGL(order_kernel, dim3(B * NH), dim3(kOrderThreads), (size_t)Nq * 4, stream,
-                       counts, order, Nq);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   if (D == 128)
     hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_units), dim3(FwdShape<128>::kThreads), 0, stream,
                        q, k, v16, list, counts, order, out, lse, max_prob, Nq, Nkv, NH,
-                       w.list_stride,
-                       scale_log2, n_units);
+                       w.list_stride, scale_log2, n_units);
   else
     hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_units), dim3(FwdShape<64>::kThreads), 0, stream,
                        q, k, v16, list, counts, order, out, lse, max_prob, Nq, Nkv, NH,
-                       w.list_stride,
-                       scale_log2, n_units);
+                       w.list_stride, scale_log2, n_units);
   return hipGetLastError();
 }
 
