@@ -15,15 +15,15 @@
 //
 // Kernels, after the selector's pool and score kernels (q and k) and one more
 // pool over v:
-//   coarse_attn_kernel  one workgroup per (16 query cubes, batch*head). Pass 1:
-//                       each wave reduces the max and the exp-sum of 4 score
-//                       rows. Pass 2: chunks of 256 key cubes; the workgroup
-//                       writes the normalised weights of the chunk to LDS, then
-//                       each lane (one channel d, a set of rows) accumulates
-//                       w[r][j] * Vc[j][d] in fp32. Vc rows are read once per
-//                       16 query cubes and are coalesced across lanes; the
-//                       weight reads are wave-wide broadcasts. A tiny
-//                       contraction (Nc^2 D per head), L2-resident.
+//   coarse_attn_kernel  one workgroup per (32 query cubes, batch*head). Pass 1:
+//                       the row maxima (loads for 8 rows in flight together,
+//                       DPP wave reductions). Pass 2, chunks of 64 key cubes:
+//                       the workgroup stages the chunk's Vc rows and weights in
+//                       LDS, and the 4 waves multiply them on fp32 MFMA
+//                       (v_mfma_f32_16x16x4_f32), each a 16-row x D/2 block;
+//                       the row sums are reduced once at the end.
+//                       A small contraction (2 Nc^2 D FLOP per head) on
+//                       L2-resident data.
 //   combine_kernel      HBM-bound elementwise pass: one workgroup per token
 //                       row, 16-byte vectors of o_fine and both gates; the
 //                       cube's O_c row (fp32) is an L2 hit shared by 64 rows.
@@ -40,97 +40,189 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // ---------------------------------------------------------------- coarse attention
 
 constexpr int kCoarseThreads = 256;  // 4 waves
-constexpr int kCoarseRows = 16;      // query cubes per workgroup
-constexpr int kChunk = kCoarseThreads;  // key cubes per LDS chunk
+constexpr int kCoarseRows = 32;      // query cubes per workgroup
+constexpr int kCoarseKeys = 64;      // key cubes per LDS chunk
+
+// Wave-wide reductions on DPP lane moves (no LDS round trips): within each
+// row of 16 lanes by quad permutes and mirrors, then across rows by the row
+// broadcasts; lane 63 ends with the result, which is read back uniformly.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp(float x, float identity) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity),
+                                                               __builtin_bit_cast(int, x), kCtrl,
+                                                               kRowMask, 0xF, false));
+}
+
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float x, float identity, Op op) {
+  x = op(x, dpp<0xB1, 0xF>(x, identity));   // quad_perm [1,0,3,2]
+  x = op(x, dpp<0x4E, 0xF>(x, identity));   // quad_perm [2,3,0,1]
+  x = op(x, dpp<0x141, 0xF>(x, identity));  // row_half_mirror
+  x = op(x, dpp<0x140, 0xF>(x, identity));  // row_mirror
+  x = op(x, dpp<0x142, 0xA>(x, identity));  // row_bcast:15 into rows 1, 3
+  x = op(x, dpp<0x143, 0xC>(x, identity));  // row_bcast:31 into rows 2, 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-  return x;
+  return wave_reduce(x, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  return wave_reduce(x, 0.0f, [](float a, float b) { return a + b; });
 }
 
-// grid (ceil(Nc / 16), B*NH). s: unscaled scores [BH][Nc][Nc]; vc, oc:
+// grid (ceil(Nc / 32), B*NH). s: unscaled scores [BH][Nc][Nc]; vc, oc:
 // [BH][Nc][D] fp32. Rows past Nc (last workgroup) read row Nc-1 and are not
 // written.
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][l/16] and B[l/16][l%16] and
+// receives D[4(l/16) + r][l%16], r = 0..3. A = the weights of 16 query rows
+// at 4 keys, B = Vc of those 4 keys at 16 channels. Wave w owns query rows
+// 16 (w % 2) .. + 15 and channels (w / 2) D/2 .. + D/2 - 1 of the tile.
 template <int D>
-__global__ __launch_bounds__(kCoarseThreads) void coarse_attn_kernel(
+__global__ __launch_bounds__(kCoarseThreads) __attribute__((amdgpu_waves_per_eu(3))) void coarse_attn_kernel(
     const float* __restrict__ s, const float* __restrict__ vc,
     const int32_t* __restrict__ vbs, float* __restrict__ oc, int Nc, float scale_log2) {
-  constexpr int kGroups = kCoarseThreads / D;     // lanes sharing one channel d
-  constexpr int kPerLane = kCoarseRows / kGroups;  // rows accumulated per lane
-  __shared__ float w[kCoarseRows][kChunk];
-  __shared__ float row_m[kCoarseRows], row_inv[kCoarseRows];
+  constexpr int kVStride = D + 16;           // floats per staged Vc row (spreads banks)
+  constexpr int kPStride = kCoarseKeys + 4;  // floats per staged weight row
+  constexpr int kCols = D / 2;               // channels per wave
+  constexpr int kBlocks = kCols / 16;        // 16-wide channel blocks per wave
+  __shared__ __attribute__((aligned(16))) float vs[kCoarseKeys * kVStride];
+  __shared__ float ps[kCoarseRows * kPStride];
+  __shared__ float row_m[kCoarseRows], row_l[kCoarseRows];
 
   const int bh = blockIdx.y, i0 = blockIdx.x * kCoarseRows;
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const float* __restrict__ sb = s + (size_t)bh * Nc * Nc;
+  const float* __restrict__ vb = vc + (size_t)bh * Nc * D;
 
-  // Pass 1: row max and sum of exp2((s - m) scale_log2) over real key cubes.
-  constexpr int kRowsPerWave = kCoarseRows / (kCoarseThreads / 64);
-  for (int rr = 0; rr < kRowsPerWave; ++rr) {
-    const int r = wave * kRowsPerWave + rr;
-    const float* __restrict__ srow = sb + (size_t)min(i0 + r, Nc - 1) * Nc;
-    float m = -INFINITY;
-    for (int j = lane; j < Nc; j += 64)
-      if (vbs[j] > 0) m = fmaxf(m, srow[j]);
-    m = wave_max(m);
-    if (m == -INFINITY) m = 0.0f;  // no real key cube: every weight is 0
-    float l = 0.0f;
-    for (int j = lane; j < Nc; j += 64)
-      if (vbs[j] > 0) l += __builtin_amdgcn_exp2f((srow[j] - m) * scale_log2);
-    l = wave_sum(l);
-    if (lane == 0) {
-      row_m[r] = m;
-      row_inv[r] = l > 0.0f ? 1.0f / l : 0.0f;
+  constexpr int kRowsPerWave = kCoarseRows / (kCoarseThreads / 64);  // row r: wave r % 4
+
+  // Pass 1: each row's max over its real key cubes. Lanes hold 4 keys of each
+  // of the wave's 8 rows per step, all 36 loads (with vbs) in flight at once.
+  {
+    float mx[kRowsPerWave];
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) mx[q] = -INFINITY;
+    for (int jb = 0; jb < Nc; jb += 4 * 64) {
+      bool real[4];
+      float v[kRowsPerWave][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + 64 * u + lane, jc = min(j, Nc - 1);
+        real[u] = j < Nc && vbs[jc] > 0;
+#pragma unroll
+        for (int q = 0; q < kRowsPerWave; ++q)
+          v[q][u] = sb[(size_t)min(i0 + wave + 4 * q, Nc - 1) * Nc + jc];
+      }
+#pragma unroll
+      for (int q = 0; q < kRowsPerWave; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mx[q] = real[u] ? fmaxf(mx[q], v[q][u]) : mx[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+      const float m = wave_max(mx[q]);
+      if (lane == 0) row_m[wave + 4 * q] = m > -INFINITY ? m : 0.0f;  // no real key: weights 0
     }
   }
   __syncthreads();
 
-  // Pass 2: o[r][d] = sum_j w[r][j] Vc[j][d].
-  const int d = threadIdx.x % D, g = threadIdx.x / D;
-  const float* __restrict__ vb = vc + (size_t)bh * Nc * D + d;
-  float acc[kPerLane];
+  // Pass 2: keys 64 at a time. The chunk's Vc rows and weights
+  // exp2((s - m) scale_log2) are staged in LDS (the wave that owns a row
+  // holds its 64 scores of the chunk, one per lane, and keeps a per-lane
+  // partial of the row's sum l); the 4 waves multiply weights by Vc on fp32
+  // MFMA. The next chunk's global loads are issued before this chunk's MFMAs.
+  // O = acc / l at the end.
+  constexpr int kVIters = kCoarseKeys * D / 4 / kCoarseThreads;  // float4 per lane
+  const int rq = 16 * (wave & 1), c0 = (wave >> 1) * kCols;
+  const int lr = lane % 16, lk = lane / 16;
+  floatx4 acc[kBlocks];
 #pragma unroll
-  for (int e = 0; e < kPerLane; ++e) acc[e] = 0.0f;
-  for (int j0 = 0; j0 < Nc; j0 += kChunk) {
-    const int j = j0 + threadIdx.x;
-    const bool real = j < Nc && vbs[j] > 0;
-#pragma unroll 4
-    for (int r = 0; r < kCoarseRows; ++r) {
-      const float sv = real ? sb[(size_t)min(i0 + r, Nc - 1) * Nc + j] : 0.0f;
-      w[r][threadIdx.x] =
-          real ? __builtin_amdgcn_exp2f((sv - row_m[r]) * scale_log2) * row_inv[r] : 0.0f;
+  for (int cb = 0; cb < kBlocks; ++cb) acc[cb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float mrow[kRowsPerWave], lpart[kRowsPerWave];
+#pragma unroll
+  for (int q = 0; q < kRowsPerWave; ++q) {
+    mrow[q] = row_m[wave + 4 * q];
+    lpart[q] = 0.0f;
+  }
+  floatx4 vreg[kVIters];
+  float sreg[kRowsPerWave];
+  // indices are clamped into range; out-of-range Vc rows become 0 and
+  // out-of-range or non-real scores -inf
+  auto load_chunk = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < kVIters; ++it) {
+      const int e = tid + kCoarseThreads * it;
+      const int key = e / (D / 4), c4 = e - key * (D / 4);
+      vreg[it] = *reinterpret_cast<const floatx4*>(vb + (size_t)min(j0 + key, Nc - 1) * D + 4 * c4);
+      if (j0 + key >= Nc) vreg[it] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int j = min(j0 + lane, Nc - 1);
+    const bool real = j0 + lane < Nc && vbs[j] > 0;
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+      const float sv = sb[(size_t)min(i0 + wave + 4 * q, Nc - 1) * Nc + j];
+      sreg[q] = real ? sv : -INFINITY;
+    }
+  };
+  load_chunk(0);
+  for (int j0 = 0; j0 < Nc; j0 += kCoarseKeys) {
+#pragma unroll
+    for (int it = 0; it < kVIters; ++it) {
+      const int e = tid + kCoarseThreads * it;
+      const int key = e / (D / 4), c4 = e - key * (D / 4);
+      *reinterpret_cast<floatx4*>(&vs[key * kVStride + 4 * c4]) = vreg[it];
+    }
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+      const float w = sreg[q] > -INFINITY ? __builtin_amdgcn_exp2f((sreg[q] - mrow[q]) * scale_log2)
+                                          : 0.0f;
+      ps[(wave + 4 * q) * kPStride + lane] = w;
+      lpart[q] += w;
     }
     __syncthreads();
-    const int n = min(kChunk, Nc - j0);
-    int jj = 0;
-    for (; jj + 8 <= n; jj += 8) {
-      float v[8];
+    if (j0 + kCoarseKeys < Nc) load_chunk(j0 + kCoarseKeys);
+    // operands of 8 key steps are read ahead of their MFMAs
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = vb[(size_t)(j0 + jj + u) * D];
+    for (int half = 0; half < 2; ++half) {
+      constexpr int kSteps = kCoarseKeys / 8;
+      float a[kSteps], b[kSteps][kBlocks];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int t = 0; t < kSteps; ++t) {
+        const int ks = half * kSteps + t;
+        a[t] = ps[(rq + lr) * kPStride + 4 * ks + lk];
 #pragma unroll
-        for (int e = 0; e < kPerLane; ++e) acc[e] = fmaf(w[g + kGroups * e][jj + u], v[u], acc[e]);
-    }
-    for (; jj < n; ++jj) {
-      const float v = vb[(size_t)(j0 + jj) * D];
+        for (int cb = 0; cb < kBlocks; ++cb) b[t][cb] = vs[(4 * ks + lk) * kVStride + c0 + 16 * cb + lr];
+      }
 #pragma unroll
-      for (int e = 0; e < kPerLane; ++e) acc[e] = fmaf(w[g + kGroups * e][jj], v, acc[e]);
+      for (int t = 0; t < kSteps; ++t)
+#pragma unroll
+        for (int cb = 0; cb < kBlocks; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t][cb], acc[cb], 0, 0, 0);
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int e = 0; e < kPerLane; ++e) {
-    const int i = i0 + g + kGroups * e;
-    if (i < Nc) oc[((size_t)bh * Nc + i) * D + d] = acc[e];
+  for (int q = 0; q < kRowsPerWave; ++q) {
+    const float l = wave_sum(lpart[q]);
+    if (lane == 0) row_l[wave + 4 * q] = l;
   }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float l = row_l[rq + 4 * lk + r];
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // no real key cube: the row is 0
+#pragma unroll
+    for (int cb = 0; cb < kBlocks; ++cb) acc[cb][r] *= inv;
+  }
+#pragma unroll
+  for (int cb = 0; cb < kBlocks; ++cb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + rq + 4 * lk + r;
+      if (i < Nc) oc[((size_t)bh * Nc + i) * D + c0 + 16 * cb + lr] = acc[cb][r];
+    }
 }
 
 // ---------------------------------------------------------------- gated combine

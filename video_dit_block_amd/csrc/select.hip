@@ -10,9 +10,10 @@
 // summaries scored by dot product).
 //
 // Three kernels on the caller's stream:
-//   pool_kernel   HBM-bound: one workgroup per (cube, batch, q|k); lanes own
-//                 16-byte column chunks of the token row and sum the cube's
-//                 real rows in fp32; the mean divides by vbs[c].
+//   pool_kernel   HBM-bound: one workgroup per (cube, 128 column chunks,
+//                 batch, tensor); each lane owns one 16-byte column chunk of
+//                 the token row and sums the cube's real rows in fp32, 8 rows
+//                 in flight; the mean divides by vbs[c].
 //   score_kernel  fp32 MFMA (v_mfma_f32_16x16x4_f32): a 64x64 tile of
 //                 S = Qc . Kc^T per workgroup. fp32 inputs keep the ranking
 //                 accurate to fp32 rounding (bf16 inputs would perturb scores
@@ -47,54 +48,65 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // ---------------------------------------------------------------- pool
 
-constexpr int kPoolThreads = 256;
+constexpr int kPoolThreads = 128;
+constexpr int kPoolUnroll = 8;  // rows in flight per lane
 
-// grid (Nc, B, 2): z = 0 pools q into qc, z = 1 pools k into kc.
+// Up to three tensors pooled by one launch; blockIdx.z picks one.
+struct PoolArgs {
+  const u32x4* x[3];
+  float* xc[3];
+};
+
+// grid (Nc * splits, B, n_tensors), splits = ceil(cpr / kPoolThreads): each
+// lane owns one 16-byte column chunk (8 channels of one head) of the cube's
+// token rows and sums its real rows in fp32, kPoolUnroll rows in flight.
 // Output layout [B][NH][Nc][D] fp32.
-__global__ __launch_bounds__(kPoolThreads) void pool_kernel(
-    const u32x4* __restrict__ q, const u32x4* __restrict__ k,
-    const int32_t* __restrict__ vbs, float* __restrict__ qc,
-    float* __restrict__ kc, int Nc, int NH, int D) {
-  const int c = blockIdx.x, b = blockIdx.y;
-  const u32x4* __restrict__ x = blockIdx.z == 0 ? q : k;
-  float* __restrict__ xc = blockIdx.z == 0 ? qc : kc;
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a, const int32_t* __restrict__ vbs,
+                                                           int Nc, int NH, int D, int splits) {
+  const int c = blockIdx.x / splits, split = blockIdx.x - c * splits, b = blockIdx.y;
   const int cpr = NH * D / 8;  // 16-byte chunks (8 bf16) per token row
+  const int col = split * kPoolThreads + threadIdx.x;
+  if (col >= cpr) return;
+  const u32x4* __restrict__ x = a.x[blockIdx.z];
+  float* __restrict__ xc = a.xc[blockIdx.z];
   const int n = min(max(vbs[c], 0), kCube);  // clamped: never reads past the cube
-  const u32x4* __restrict__ base = x + ((size_t)b * Nc + c) * kCube * cpr;
-  for (int col = threadIdx.x; col < cpr; col += kPoolThreads) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int u = 0;
-    for (; u + 3 < n; u += 4) {
-      u32x4 t[4];
+  const u32x4* __restrict__ base = x + ((size_t)b * Nc + c) * kCube * cpr + col;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  auto add = [&](const u32x4 t) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t[i] = base[(size_t)(u + i) * cpr + col];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += __uint_as_float(t[i][e] << 16);
-          acc[2 * e + 1] += __uint_as_float(t[i][e] & 0xFFFF0000u);
-        }
-    }
-    for (; u < n; ++u) {
-      const u32x4 t = base[(size_t)u * cpr + col];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += __uint_as_float(t[e] << 16);
-        acc[2 * e + 1] += __uint_as_float(t[e] & 0xFFFF0000u);
-      }
-    }
-    const int elem = col * 8;
-    const int h = elem / D, d = elem - h * D;
-    float* dst = xc + (((size_t)b * NH + h) * Nc + c) * D + d;
-    floatx4 lo, hi;
     for (int e = 0; e < 4; ++e) {
-      lo[e] = n > 0 ? acc[e] / (float)n : 0.0f;
-      hi[e] = n > 0 ? acc[4 + e] / (float)n : 0.0f;
+      acc[2 * e] += __uint_as_float(t[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(t[e] & 0xFFFF0000u);
     }
-    *reinterpret_cast<floatx4*>(dst) = lo;
-    *reinterpret_cast<floatx4*>(dst + 4) = hi;
+  };
+  int u = 0;
+  for (; u + kPoolUnroll <= n; u += kPoolUnroll) {
+    u32x4 t[kPoolUnroll];
+#pragma unroll
+    for (int i = 0; i < kPoolUnroll; ++i) t[i] = __builtin_nontemporal_load(base + (size_t)(u + i) * cpr);
+#pragma unroll
+    for (int i = 0; i < kPoolUnroll; ++i) add(t[i]);
   }
+  for (; u < n; ++u) add(__builtin_nontemporal_load(base + (size_t)u * cpr));
+  const int elem = col * 8;
+  const int h = elem / D, d = elem - h * D;
+  float* dst = xc + (((size_t)b * NH + h) * Nc + c) * D + d;
+  floatx4 lo, hi;
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = n > 0 ? acc[e] / (float)n : 0.0f;
+    hi[e] = n > 0 ? acc[4 + e] / (float)n : 0.0f;
+  }
+  *reinterpret_cast<floatx4*>(dst) = lo;
+  *reinterpret_cast<floatx4*>(dst + 4) = hi;
+}
+
+hipError_t pool_launch(const PoolArgs& a, int n_tensors, const int32_t* vbs, int B, int Nc,
+                       int NH, int D, hipStream_t stream) {
+  const int cpr = NH * D / 8;
+  const int splits = (cpr + kPoolThreads - 1) / kPoolThreads;
+  hipLaunchKernelGGL(pool_kernel, dim3(Nc * splits, B, n_tensors), dim3(kPoolThreads), 0, stream,
+                     a, vbs, Nc, NH, D, splits);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- scores
@@ -127,19 +139,24 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
     const floatx4 v = *reinterpret_cast<const floatx4*>(qb + (size_t)qi * D + g * kSeg + t);
     a[t] = v[0]; a[t + 1] = v[1]; a[t + 2] = v[2]; a[t + 3] = v[3];
   }
-#pragma unroll 1
-  for (int cb = 0; cb < kScoreTile / 16; ++cb) {
+  // Kc rows of column block cb, loaded one block ahead of its MFMA chain
+  float bv[2][kSeg];
+  auto load_b = [&](int cb, float* dst) __attribute__((always_inline)) {
     const int kj = min(j0 + 16 * cb + r, Nc - 1);
-    float bv[kSeg];
 #pragma unroll
     for (int t = 0; t < kSeg; t += 4) {
       const floatx4 v = *reinterpret_cast<const floatx4*>(kb + (size_t)kj * D + g * kSeg + t);
-      bv[t] = v[0]; bv[t + 1] = v[1]; bv[t + 2] = v[2]; bv[t + 3] = v[3];
+      dst[t] = v[0]; dst[t + 1] = v[1]; dst[t + 2] = v[2]; dst[t + 3] = v[3];
     }
+  };
+  load_b(0, bv[0]);
+#pragma unroll
+  for (int cb = 0; cb < kScoreTile / 16; ++cb) {
+    if (cb + 1 < kScoreTile / 16) load_b(cb + 1, bv[(cb + 1) & 1]);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < kSeg; ++t)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], bv[t], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], bv[cb & 1][t], acc, 0, 0, 0);
     const int col = j0 + 16 * cb + r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -396,10 +413,10 @@ __global__ __launch_bounds__(64 * kWaveRowsMax) void topk_wave_kernel(
 
 hipError_t launch_pool(const uint16_t* x_tiled, const int32_t* vbs, int B, int Nc, int NH,
                        int D, float* xc, hipStream_t stream) {
-  hipLaunchKernelGGL(pool_kernel, dim3(Nc, B, 1), dim3(kPoolThreads), 0, stream,
-                     reinterpret_cast<const u32x4*>(x_tiled),
-                     reinterpret_cast<const u32x4*>(x_tiled), vbs, xc, xc, Nc, NH, D);
-  return hipGetLastError();
+  PoolArgs a = {};
+  a.x[0] = reinterpret_cast<const u32x4*>(x_tiled);
+  a.xc[0] = xc;
+  return pool_launch(a, 1, vbs, B, Nc, NH, D, stream);
 }
 
 SelectWorkspace select_workspace(int B, int NH, int Nc, int D) {
@@ -421,10 +438,12 @@ hipError_t launch_pool_scores(const uint16_t* q_tiled, const uint16_t* k_tiled,
   float* kc = reinterpret_cast<float*>(ws + w.kc_off);
   float* s = reinterpret_cast<float*>(ws + w.s_off);
 
-  hipLaunchKernelGGL(pool_kernel, dim3(Nc, B, 2), dim3(kPoolThreads), 0, stream,
-                     reinterpret_cast<const u32x4*>(q_tiled),
-                     reinterpret_cast<const u32x4*>(k_tiled), vbs, qc, kc, Nc, NH, D);
-  hipError_t e = hipGetLastError();
+  PoolArgs a = {};
+  a.x[0] = reinterpret_cast<const u32x4*>(q_tiled);
+  a.x[1] = reinterpret_cast<const u32x4*>(k_tiled);
+  a.xc[0] = qc;
+  a.xc[1] = kc;
+  hipError_t e = pool_launch(a, 2, vbs, B, Nc, NH, D, stream);
   if (e != hipSuccess) return e;
 
   const int nt = (Nc + kScoreTile - 1) / kScoreTile;
