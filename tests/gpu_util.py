@@ -281,3 +281,18 @@ def combine_check(out_bits, o_fine_bits, o_coarse, gc_bits, gf_bits, label: str)
     print(f"[{label}] equal to the rounded exact value: {n_eq}/{got.size}; worst |d| / bound "
           f"{ratio.max():.6f}", flush=True)
     assert np.all(ratio <= 1.0), label
+
+
+def stat_tolerance_rows(q_rows, k_all, ids, vbs, scale):
+    """Per query row, the bound on |d lse| of the fine kernel (and on the
+    relative error of max_prob, halved): l is the fp32 sum of fp16-rounded
+    weights (2^-11 + n 2^-24 relative), and each score is an fp32 MFMA dot
+    product of bf16 inputs (|d s| <= gamma_D sum_d |q_d k_d|, Higham), which
+    moves lse by at most twice that times sm_scale. q_rows (64, D) and k_all
+    (S, D) are float64 tiled rows of one (b, h)."""
+    rows = np.concatenate([64 * j + np.arange(vbs[j]) for j in ids]) if len(ids) else np.zeros(0, int)
+    if rows.size == 0:
+        return np.zeros(q_rows.shape[0])
+    D = q_rows.shape[-1]
+    a = np.abs(q_rows) @ np.abs(k_all[rows]).T
+    return 2.0 ** -11 + rows.size * 2.0 ** -24 + 2 * gamma(D) * scale * a.max(axis=1)
