@@ -5,7 +5,8 @@ heavy-tailed q/k with one high-logit head. The whole path runs on the device:
 tiling (bit-exact), the selector (every row), the fine stage on the oracle's
 indices (finite everywhere; every head x 16 seeded query cubes plus 64 cubes of
 the outlier head against the oracle) and untiling (the exact inverse of the
-tiling on every real token)."""
+tiling on every real token); the cumulative-mass selector and the coarse
+output on every row."""
 import numpy as np
 import pytest
 import torch
@@ -53,3 +54,27 @@ def test_untile_inverts_tile(run):
     c = run.case
     back = run.vsa.untile(run.vt, c.T, c.H, c.W)
     np.testing.assert_array_equal(from_gpu_bf16(back), c.v)
+
+
+def test_cdf_counts_and_coarse_every_row(run):
+    """The cumulative-mass selector (tau 0.9, at most half of the cubes) on
+    every one of the 46,080 rows against the fp64 scores, and the coarse
+    output on every (head, cube)."""
+    import math
+
+    import oracle
+    from gpu_util import check_coarse
+    from test_gpu_7_cdf import _check_counts, _score_err
+
+    idx_o, S, Qc, Kc, Qa, Ka = run.oracle_select()
+    D, Nc = run.case.D, run.Nc
+    scale, max_k, tau = 1 / math.sqrt(D), Nc // 2, 0.9
+    gidx, gcnt = run.vsa.select_cdf(run.qt, run.kt, run.vbs, max_k, tau)
+    gidx, gcnt = gidx.cpu().numpy(), gcnt.cpu().numpy()
+    _, ora_cnt = oracle.cdf_counts(S, max_k, tau, scale)
+    bad = _check_counts(gidx, gcnt, S, _score_err(Qc, Kc, Qa, Ka, 64), tau, scale, max_k)
+    print(f"[hy720 cdf] mean count {gcnt.mean():.1f} (oracle {ora_cnt.mean():.1f}), equal "
+          f"counts {int((gcnt == ora_cnt).sum())}/{gcnt.size}, invalid {bad}", flush=True)
+    assert bad == 0
+    oc = run.vsa.coarse(run.qt, run.kt, run.vt, run.vbs)
+    check_coarse(oc.cpu().numpy(), run.head64, run.vbs_o, run.case.NH, None, "hy720 coarse")
