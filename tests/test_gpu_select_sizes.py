@@ -28,7 +28,8 @@ def _cube_constant(Nc, NH, D, levels, rng):
     return synth.bf16_bits_from_f32(np.repeat(vec, 64, axis=0)[None])
 
 
-@pytest.mark.parametrize("Nc", [1, 8, 64, 65, 128, 129, 256, 640, 1024, 1025, 2048, 2049, 2100])
+@pytest.mark.parametrize("Nc", [1, 8, 64, 65, 128, 129, 256, 640, 1024, 1025, 2048, 2049, 2100,
+                                4096, 8192])
 def test_topk_exact_scores_every_size(Nc):
     rng = np.random.default_rng(Nc)
     NH, D = 2, 64
