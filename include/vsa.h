@@ -214,8 +214,9 @@ size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
  * topk_idx[b, h, c, :]. q.k^T runs on bf16 inputs with fp32 accumulation;
  * the softmax is computed online in fp32 with a running row maximum
  * subtracted; the weights and V enter the P.V product as fp16 (V is exact in
- * fp16 for |v| <= 65504, larger magnitudes saturate to 65504) with fp32
- * accumulation; the output is rounded to bf16 (nearest even). A row with no
+ * fp16 for 2^-14 <= |v| <= 65504 and 0; larger magnitudes saturate to 65504,
+ * smaller ones are truncated toward zero, an absolute error under 2^-24) with
+ * fp32 accumulation; the output is rounded to bf16 (nearest even). A row with no
  * real key outputs 0.
  *   q         [B][Nq*64][NH][D] bf16, tiled order (padding rows are computed
  *             like real rows)

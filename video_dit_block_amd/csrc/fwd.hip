@@ -67,9 +67,10 @@
 //   runs as an fp16 MFMA (v_mfma_f32_32x32x16_f16): P is rounded to fp16 and
 //   V is converted to fp16 by the pre-pass. fp16 keeps 3 more
 //   significand bits than bf16, which matters for rows with few keys; V is
-//   converted exactly for |v| <= 65504 (bf16 values are a subset of fp16 in
-//   that range) and saturates to 65504 beyond it. O / l is rounded to bf16
-//   (nearest even) and stored.
+//   converted exactly for 2^-14 <= |v| <= 65504 and 0 (there every bf16
+//   value is an fp16 value), saturates to 65504 above, and below 2^-14 (fp16
+//   subnormals) is truncated toward zero, an absolute error under 2^-24. O / l
+//   is rounded to bf16 (nearest even) and stored.
 #include <type_traits>
 
 #include "device.h"
@@ -186,11 +187,22 @@ using IC = std::integral_constant<int, N>;
 // ---------------------------------------------------------------------------
 // V -> fp16 pre-pass. Writes an fp16 copy of v (same tiled BSHD layout) into
 // the workspace: real rows converted, padding rows zeroed. bf16 -> f32 is
-// exact (the bf16 bits are the upper half of an f32); f32 -> f16 truncation
-// is exact for |v| <= 65504, since every such bf16 value is an fp16 value,
-// and saturates to 65504 beyond. HBM-bound: one read and one write of v.
+// exact (the bf16 bits are the upper half of an f32); f32 -> f16 with
+// truncation is exact for 2^-14 <= |v| <= 65504 and 0, since every such bf16
+// value is an fp16 value; it saturates to 65504 above, and below 2^-14 (fp16
+// subnormals) it loses at most 2^-24. HBM-bound: one read and one write of v.
 constexpr int kCvtThreads = 256;
-constexpr int kCvtSplit = 4;  // workgroups per cube (16 slots each)
+constexpr int kCvtSplit = 8;   // workgroups per cube (8 slots each)
+constexpr int kCvtUnroll = 8;  // 16-byte loads in flight per lane
+
+__device__ __forceinline__ u32x4 bf16x8_to_fp16x8(const u32x4 w) {
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[e] << 16),
+                                                                  __uint_as_float(w[e] & 0xFFFF0000u)));
+  return o;
+}
 
 __global__ __launch_bounds__(kCvtThreads) void v_to_fp16_kernel(
     const u32x4* __restrict__ v, u32x4* __restrict__ v16, const int32_t* __restrict__ vbs,
@@ -205,16 +217,15 @@ __global__ __launch_bounds__(kCvtThreads) void v_to_fp16_kernel(
     const u32x4* __restrict__ src = v + row * cpr;
     u32x4* __restrict__ dst = v16 + row * cpr;
     if (u < nv) {
-      for (int col = lane; col < cpr; col += 64) {
-        const u32x4 w = src[col];
-        u32x4 o;
+      int col = lane;
+      for (; col + 64 * (kCvtUnroll - 1) < cpr; col += 64 * kCvtUnroll) {
+        u32x4 w[kCvtUnroll];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
-                                                   __uint_as_float(w[e] << 16),
-                                                   __uint_as_float(w[e] & 0xFFFF0000u)));
-        dst[col] = o;
+        for (int i = 0; i < kCvtUnroll; ++i) w[i] = __builtin_nontemporal_load(src + col + 64 * i);
+#pragma unroll
+        for (int i = 0; i < kCvtUnroll; ++i) dst[col + 64 * i] = bf16x8_to_fp16x8(w[i]);
       }
+      for (; col < cpr; col += 64) dst[col] = bf16x8_to_fp16x8(__builtin_nontemporal_load(src + col));
     } else {
       const u32x4 z = {0u, 0u, 0u, 0u};
       for (int col = lane; col < cpr; col += 64) dst[col] = z;

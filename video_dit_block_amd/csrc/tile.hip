@@ -8,7 +8,7 @@
 //
 // In BSHD the NH*D values of one token are contiguous (NH*D*2 bytes: 10 KiB
 // for 40 heads of 128), so tiling is a gather of whole token rows. Each
-// workgroup moves 16 slots of one cube; each wave copies one row at a time
+// workgroup moves 8 slots of one cube; each wave copies one row at a time
 // with 16-byte accesses across its 64 lanes, so every access instruction
 // covers 1 KiB of contiguous memory. Padding slots are written as zeros and
 // never read. The work is a pure copy and is bound by HBM bandwidth.
@@ -35,10 +35,10 @@
 namespace vsa {
 namespace {
 
-constexpr int kSlotsPerBlock = 16;
+constexpr int kSlotsPerBlock = 8;
 constexpr int kSplit = kCube / kSlotsPerBlock;  // workgroups per cube
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 // Copy one row of `cpr` 16-byte chunks (src == nullptr: write zeros).
 __device__ __forceinline__ void copy_row(const u32x4* __restrict__ src,
