@@ -249,21 +249,39 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int b = row / rows_per_b, c = (row - b * rows_per_b) / kCube;
   const int cpr = NH * D / 8;  // 16-byte chunks per token row
   const size_t base = (size_t)row * cpr;
-  for (int col = threadIdx.x; col < cpr; col += kCombineThreads) {
-    const int h = col / (D / 8), d = (col % (D / 8)) * 8;
-    const float* ocp = oc + (((size_t)b * NH + h) * Nc + c) * D + d;
-    const floatx4 lo = *reinterpret_cast<const floatx4*>(ocp);
-    const floatx4 hi = *reinterpret_cast<const floatx4*>(ocp + 4);
-    const float o8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const u32x4 f = o_fine[base + col], a = gate_c[base + col], z = gate_f[base + col];
-    u32x4 r;
+  // kBatch chunks per lane are loaded before any is stored (out may alias an
+  // input, so loads cannot be moved above earlier stores by the compiler);
+  // this keeps 3 x kBatch 16-byte loads in flight per lane
+  constexpr int kBatch = 4;
+  for (int col0 = threadIdx.x; col0 < cpr; col0 += kBatch * kCombineThreads) {
+    u32x4 f[kBatch], a[kBatch], z[kBatch];
+    floatx4 lo[kBatch], hi[kBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x0 = fmaf(bf16_lo(a[e]), o8[2 * e], bf16_lo(z[e]) * bf16_lo(f[e]));
-      const float x1 = fmaf(bf16_hi(a[e]), o8[2 * e + 1], bf16_hi(z[e]) * bf16_hi(f[e]));
-      r[e] = pack_bf16x2(x0, x1);
+    for (int i = 0; i < kBatch; ++i) {
+      const int col = min(col0 + i * kCombineThreads, cpr - 1);
+      const int h = col / (D / 8), d = (col % (D / 8)) * 8;
+      const float* ocp = oc + (((size_t)b * NH + h) * Nc + c) * D + d;
+      lo[i] = *reinterpret_cast<const floatx4*>(ocp);
+      hi[i] = *reinterpret_cast<const floatx4*>(ocp + 4);
+      f[i] = o_fine[base + col];
+      a[i] = gate_c[base + col];
+      z[i] = gate_f[base + col];
     }
-    out[base + col] = r;
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int col = col0 + i * kCombineThreads;
+      if (col >= cpr) break;
+      const float o8[8] = {lo[i][0], lo[i][1], lo[i][2], lo[i][3],
+                           hi[i][0], hi[i][1], hi[i][2], hi[i][3]};
+      u32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = fmaf(bf16_lo(a[i][e]), o8[2 * e], bf16_lo(z[i][e]) * bf16_lo(f[i][e]));
+        const float x1 = fmaf(bf16_hi(a[i][e]), o8[2 * e + 1], bf16_hi(z[i][e]) * bf16_hi(f[i][e]));
+        r[e] = pack_bf16x2(x0, x1);
+      }
+      out[base + col] = r;
+    }
   }
 }
 
