@@ -23,12 +23,13 @@
 //   one XCD walk their head's key/value cubes in the same order.
 // * One workgroup = one unit: 2 waves of 32 query rows, 4 workgroups per CU
 //   (2 waves per SIMD; 32 KiB of LDS each). Units are numbered head-major and
-//   remapped so each XCD walks a contiguous range. With per-row counts (a
-//   lookup table) a third pre-pass orders each head's query cubes by
-//   descending count, and that order is the dispatch order inside the head: with mixed lengths in flight, the short units race ahead through
-//   the key cubes and the L2 reuse between neighbours is lost (measured on
-//   the Wan tensors at a 0.9 mass threshold: 18.5 -> 14.1 ms). Equal counts
-//   keep the plain order, which is the better one then.
+//   remapped so each XCD walks a contiguous range. A third pre-pass orders
+//   each head's query cubes by descending count of selected cubes, then by
+//   ascending smallest selected id, and that order is the dispatch order
+//   inside the head. Units that run side by side then start their ascending
+//   sweeps close together and move at similar rates, so they keep sharing L2
+//   lines (measured on the Wan tensors: top-78 4.23 -> 3.99 ms; a lookup
+//   table at a 0.9 mass threshold 18.5 -> 14.1 ms).
 // * K and V half-tiles stream through LDS, each double-buffered, loaded
 //   global -> LDS directly (buffer_load ... lds, two 1 KiB loads per M0
 //   write); every wave loads half of each tile. The buffer range of a load
@@ -305,29 +306,36 @@ __global__ __launch_bounds__(64) void halves_kernel(
   if (lane == 0) counts[unit] = base;
 }
 
-// Dispatch order of a lookup table with per-row counts: per (b, h), the query
-// cubes by descending count of selected cubes (ties by cube id, so equal
-// counts keep the spatial order). Units of one head that run side by side
-// then carry similar amounts of work, so they sweep the key cubes at similar
-// rates (their accesses stay close together in L2), and the longest units
-// start first. grid (B*NH), dynamic LDS Nq int32.
-constexpr int kOrderThreads = 256;
+// Dispatch order inside each (b, h): query cubes by descending count of
+// selected cubes, then by ascending smallest selected id, then by cube id.
+// Units that run side by side then sweep the ascending key ids from nearby
+// starting points at similar rates, so their half-tile loads keep hitting the
+// same L2 lines, and with per-row counts the longest units start first.
+// grid (B*NH), one thread per query cube; dynamic LDS 2 Nq int32.
+constexpr int kOrderThreads = 1024;
 constexpr int kOrderMaxNq = 4096;
 
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(const int32_t* __restrict__ valid,
-                                                              int row_len,
-                                                              int32_t* __restrict__ order, int Nq) {
-  extern __shared__ int32_t cnt[];
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ valid, int row_len,
+    int Nkv, int32_t* __restrict__ order, int Nq) {
+  extern __shared__ int32_t key[];  // (count, smallest id) per query cube
   const size_t base = (size_t)blockIdx.x * Nq;
-  for (int i = threadIdx.x; i < Nq; i += kOrderThreads)
-    cnt[i] = min(max(valid[base + i], 0), row_len);
+  for (int i = threadIdx.x; i < Nq; i += kOrderThreads) {
+    const int n = valid == nullptr ? row_len : min(max(valid[base + i], 0), row_len);
+    const int32_t* __restrict__ sel = topk_idx + (base + i) * row_len;
+    int first = 0x7FFFFFFF;
+#pragma unroll 8
+    for (int t = 0; t < n; ++t) first = min(first, min(max(sel[t], 0), Nkv - 1));
+    key[2 * i] = n;
+    key[2 * i + 1] = first;
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < Nq; i += kOrderThreads) {
-    const int ci = cnt[i];
+    const int ci = key[2 * i], fi = key[2 * i + 1];
     int rank = 0;
     for (int j = 0; j < Nq; ++j) {
-      const int cj = cnt[j];
-      rank += (cj > ci) | ((cj == ci) & (j < i));
+      const int cj = key[2 * j], fj = key[2 * j + 1];
+      rank += (cj > ci) | ((cj == ci) & ((fj < fi) | ((fj == fi) & (j < i))));
     }
     order[base + rank] = i;
   }
@@ -688,10 +696,10 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // The order pass runs ahead of the list pass: launched right before the
   // fine kernel it cost that kernel about 1 ms at 312 cubes per row
   // (measured, cause not established).
-  if (valid != nullptr && Nq <= kOrderMaxNq) {
+  if (Nq <= kOrderMaxNq) {
     order = reinterpret_cast<int32_t*>(ws + w.order_off);
-    hipLaunchKernelGGL(order_kernel, dim3(B * NH), dim3(kOrderThreads), (size_t)Nq * 4, stream,
-                       valid, topk, order, Nq);
+    hipLaunchKernelGGL(order_kernel, dim3(B * NH), dim3(kOrderThreads), (size_t)Nq * 8, stream,
+                       topk_idx, valid, topk, Nkv, order, Nq);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
