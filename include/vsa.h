@@ -199,8 +199,8 @@ int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
  * in the tiled layout (B * Nkv * 64 * NH * D * 2 bytes), then, per (b, h,
  * query cube) (B * NH * Nq of them), the list of the 32-token halves that
  * hold real tokens of its selected cubes ((2 * topk + 4) entries of two
- * uint32), its length (one int32) and its dispatch rank (one int32, used by
- * vsa_fwd_lut with per-row counts), each part 256-byte aligned. Returns 0 for
+ * uint32), its length (one int32), its dispatch rank (one int32) and the
+ * rank's sort key (two int32), each part 256-byte aligned. Returns 0 for
  * invalid sizes. */
 size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
                                int32_t D, int32_t topk);

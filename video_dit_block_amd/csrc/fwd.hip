@@ -311,34 +311,47 @@ __global__ __launch_bounds__(64) void halves_kernel(
 // Units that run side by side then sweep the ascending key ids from nearby
 // starting points at similar rates, so their half-tile loads keep hitting the
 // same L2 lines, and with per-row counts the longest units start first.
-// grid (B*NH), one thread per query cube; dynamic LDS 2 Nq int32.
-constexpr int kOrderThreads = 1024;
+// Two passes: order_key_kernel writes one packed key per unit, a lane quad
+// per unit; order_rank_kernel ranks each head's keys, grid (B*NH,
+// ceil(Nq / 256)), dynamic LDS Nq uint64. Smallest ids are capped at 2^20 - 1
+// in the key (the order stays valid, only less sharp, above that).
+constexpr int kOrderThreads = 256;
 constexpr int kOrderMaxNq = 4096;
 
-__global__ __launch_bounds__(kOrderThreads) void order_kernel(
+// The key packs the order into one integer: 2^31 - 1 - count, then the
+// smallest id (below 2^20), then the cube id (below kOrderMaxNq = 2^12).
+__global__ __launch_bounds__(kOrderThreads) void order_key_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ valid, int row_len,
-    int Nkv, int32_t* __restrict__ order, int Nq) {
-  extern __shared__ int32_t key[];  // (count, smallest id) per query cube
-  const size_t base = (size_t)blockIdx.x * Nq;
-  for (int i = threadIdx.x; i < Nq; i += kOrderThreads) {
-    const int n = valid == nullptr ? row_len : min(max(valid[base + i], 0), row_len);
-    const int32_t* __restrict__ sel = topk_idx + (base + i) * row_len;
-    int first = 0x7FFFFFFF;
+    int Nkv, int Nq, uint64_t* __restrict__ keys, int64_t n_units) {
+  const int64_t i4 = (int64_t)blockIdx.x * kOrderThreads + threadIdx.x;
+  const int64_t unit = i4 >> 2;
+  const int part = (int)(i4 & 3);
+  if (unit >= n_units) return;  // whole quads leave together (n_units * 4 lanes)
+  const int n = valid == nullptr ? row_len : min(max(valid[unit], 0), row_len);
+  const int32_t* __restrict__ sel = topk_idx + unit * row_len;
+  int first = (1 << 20) - 1;
 #pragma unroll 8
-    for (int t = 0; t < n; ++t) first = min(first, min(max(sel[t], 0), Nkv - 1));
-    key[2 * i] = n;
-    key[2 * i + 1] = first;
-  }
+  for (int t = part; t < n; t += 4) first = min(first, min(max(sel[t], 0), Nkv - 1));
+  first = min(first, __shfl_xor(first, 1, 64));
+  first = min(first, __shfl_xor(first, 2, 64));
+  if (part == 0)
+    keys[unit] = ((uint64_t)(0x7FFFFFFF - n) << 32) | ((uint64_t)first << 12) |
+                 (uint64_t)(unit % Nq);
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_rank_kernel(
+    const uint64_t* __restrict__ keys, int32_t* __restrict__ order, int Nq) {
+  extern __shared__ uint64_t key[];
+  const size_t base = (size_t)blockIdx.x * Nq;
+  for (int i = threadIdx.x; i < Nq; i += kOrderThreads) key[i] = keys[base + i];
   __syncthreads();
-  for (int i = threadIdx.x; i < Nq; i += kOrderThreads) {
-    const int ci = key[2 * i], fi = key[2 * i + 1];
-    int rank = 0;
-    for (int j = 0; j < Nq; ++j) {
-      const int cj = key[2 * j], fj = key[2 * j + 1];
-      rank += (cj > ci) | ((cj == ci) & ((fj < fi) | ((fj == fi) & (j < i))));
-    }
-    order[base + rank] = i;
-  }
+  const int i = blockIdx.y * kOrderThreads + threadIdx.x;
+  if (i >= Nq) return;
+  const uint64_t ki = key[i];
+  int rank = 0;  // keys are distinct (the cube id is part of them)
+#pragma unroll 8
+  for (int j = 0; j < Nq; ++j) rank += key[j] < ki;
+  order[base + rank] = i;
 }
 
 // ---------------------------------------------------------------------------
@@ -671,7 +684,8 @@ FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk) {
   w.list_off = up((size_t)B * Nkv * kCube * NH * D * 2);
   w.count_off = w.list_off + up(units * w.list_stride * 8);
   w.order_off = w.count_off + up(units * 4);
-  w.total = w.order_off + up(units * 4);
+  w.key_off = w.order_off + up(units * 4);
+  w.total = w.key_off + up(units * 8);
   return w;
 }
 
@@ -698,8 +712,15 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   // (measured, cause not established).
   if (Nq <= kOrderMaxNq) {
     order = reinterpret_cast<int32_t*>(ws + w.order_off);
-    hipLaunchKernelGGL(order_kernel, dim3(B * NH), dim3(kOrderThreads), (size_t)Nq * 8, stream,
-                       topk_idx, valid, topk, Nkv, order, Nq);
+    uint64_t* keys = reinterpret_cast<uint64_t*>(ws + w.key_off);
+    const int64_t lanes = (int64_t)n_units * 4;
+    hipLaunchKernelGGL(order_key_kernel, dim3((unsigned)((lanes + kOrderThreads - 1) / kOrderThreads)),
+                       dim3(kOrderThreads), 0, stream, topk_idx, valid, topk, Nkv, Nq, keys,
+                       (int64_t)n_units);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(order_rank_kernel, dim3(B * NH, (Nq + kOrderThreads - 1) / kOrderThreads),
+                       dim3(kOrderThreads), (size_t)Nq * sizeof(uint64_t), stream, keys, order, Nq);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

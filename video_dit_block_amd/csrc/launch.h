@@ -65,9 +65,9 @@ hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
 
 // Workspace carve-up of vsa_fwd: an fp16 copy of v in the tiled layout, the
 // half-tile lists of the units ([B*NH*Nq][list_stride] pairs of uint32), their
-// lengths, and the dispatch order used with per-row counts.
+// lengths, the dispatch order and its sort keys.
 struct FwdWorkspace {
-  size_t v16_off, list_off, count_off, order_off, total;
+  size_t v16_off, list_off, count_off, order_off, key_off, total;
   int list_stride;
 };
 FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk);
