@@ -276,6 +276,14 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     fwd_ms = e0.elapsed_time(e1) / args.fwd_reps
+    # the same calls one at a time, each between its own pair of events
+    pairs = [(ev(), ev()) for _ in range(args.fwd_reps)]
+    for a, b in pairs:
+        a.record()
+        vsa.fwd(qt, kt, vt, idx, vbs, out=out, workspace=wsf)
+        b.record()
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in pairs])
 
     vbs_h = vbs.cpu().numpy()
     idx_h = idx.cpu().numpy()
@@ -460,6 +468,10 @@ def main():
             "parallelism": "single GPU",
         },
         "fwd_ms": round(fwd_ms, 4),
+        "fwd_ms_per_call": {"p10": round(float(np.percentile(per_call, 10)), 4),
+                            "median": round(float(np.median(per_call)), 4),
+                            "p90": round(float(np.percentile(per_call, 90)), 4),
+                            "calls": int(per_call.size)},
         "fwd_tflop": round(flops / 1e12, 4),
         "fwd_pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "fwd_finite": finite,
