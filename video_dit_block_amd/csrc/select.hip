@@ -16,7 +16,7 @@
 //                 in flight; the mean divides by vbs[c].
 //   score_kernel  fp32 MFMA (v_mfma_f32_16x16x4_f32): a 64x64 tile of
 //                 S = Qc . Kc^T per workgroup, its 64 Kc rows staged once in
-//                 LDS for the four waves (Wan shape: 59 us, against 91 us
+//                 LDS for the four waves (Wan shape: 57-62 us, against 91-97 us
 //                 with every wave reading its Kc operands from L2). fp32
 //                 inputs keep the ranking accurate to fp32 rounding (bf16
 //                 inputs would perturb scores by ~2^-9 relative and reorder
