@@ -67,7 +67,7 @@ def small():
     return ConfigRun(synth.small())
 
 
-@pytest.mark.parametrize("tau,max_k", [(0.5, 624), (0.9, 312), (0.99, 187)])
+@pytest.mark.parametrize("tau,max_k", [(0.5, 624), (0.9, 312), (0.99, 187), (0.5, 128), (0.9, 100)])
 def test_select_cdf_small_every_row(small, tau, max_k):
     idx_o, S, Qc, Kc, Qa, Ka = small.oracle_select()
     D = Qc.shape[-1]
