@@ -267,6 +267,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 
 constexpr int kWaveRowsMax = 4;  // rows (waves) per workgroup
 
+// Inclusive prefix sum over the wave on DPP lane moves (no LDS round trips):
+// within each row of 16 lanes by shifts of 1, 2, 4 and 8 (a lane without a
+// source adds 0), then across rows by the row broadcasts of lanes 15 and 31.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 into rows 1, 3
+  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -315,12 +333,8 @@ __global__ __launch_bounds__(64 * kWaveRowsMax) void topk_wave_kernel(
     const uint32_t b0 = bins[4 * lane], b1 = bins[4 * lane + 1], b2 = bins[4 * lane + 2],
                    b3 = bins[4 * lane + 3];
     const uint32_t t = b0 + b1 + b2 + b3;
-    uint32_t suf = t;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(suf, off, 64);
-      if (lane + off < 64) suf += o;
-    }
+    const uint32_t pre = wave_prefix_sum(t);  // keys with digit < 4 (l + 1)
+    const uint32_t suf = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63) - pre + t;
     // the digit d is the largest with (keys with digit >= d) >= krem; its lane
     // is the one lane with suf >= krem > suf - t
     const uint64_t hit = __ballot(suf >= krem && suf - t < krem);
@@ -338,8 +352,8 @@ __global__ __launch_bounds__(64 * kWaveRowsMax) void topk_wave_kernel(
         d = 4 * L; above = c1;
       }
     }
-    d = __shfl(d, L, 64);
-    above = __shfl(above, L, 64);
+    d = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
     krem -= above;
     prefix |= d << shift;
     pmask |= 0xFFu << shift;
