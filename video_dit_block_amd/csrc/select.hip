@@ -339,35 +339,40 @@ __global__ __launch_bounds__(64 * kWaveRowsMax) void topk_wave_kernel(
     // is the one lane with suf >= krem > suf - t
     const uint64_t hit = __ballot(suf >= krem && suf - t < krem);
     const int L = __ffsll((unsigned long long)hit) - 1;
-    uint32_t d = 0, above = 0;  // above = keys with digit > d
+    uint32_t d = 0, above = 0, at = 0;  // above / at: keys with digit > d / == d
     if (lane == L) {
       const uint32_t c4 = suf - t, c3 = c4 + b3, c2 = c3 + b2, c1 = c2 + b1;
       if (c3 >= krem) {
-        d = 4 * L + 3; above = c4;
+        d = 4 * L + 3; above = c4; at = b3;
       } else if (c2 >= krem) {
-        d = 4 * L + 2; above = c3;
+        d = 4 * L + 2; above = c3; at = b2;
       } else if (c1 >= krem) {
-        d = 4 * L + 1; above = c2;
+        d = 4 * L + 1; above = c2; at = b1;
       } else {
-        d = 4 * L; above = c1;
+        d = 4 * L; above = c1; at = b0;
       }
     }
     d = (uint32_t)__builtin_amdgcn_readlane((int)d, L);
     above = (uint32_t)__builtin_amdgcn_readlane((int)above, L);
+    at = (uint32_t)__builtin_amdgcn_readlane((int)at, L);
     krem -= above;
     prefix |= d << shift;
     pmask |= 0xFFu << shift;
+    // every key sharing the prefix belongs to the top k: the lower digits
+    // need not be resolved (and no tie among them needs breaking)
+    if (at == krem) break;
   }
 
-  // Compact the top k: keys above the threshold, then the krem lowest-id keys
-  // equal to it (ids ascend with (i, lane)).
+  // Compact the top k: keys whose resolved bits are above the prefix, then
+  // the krem lowest-id keys equal to it on those bits (ids ascend with
+  // (i, lane)); after an early exit that is every key equal to it.
   const int n_gt = topk - (int)krem;
   int seen_gt = 0, seen_eq = 0;
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int j = 64 * i + lane;
     const bool ok = j < Nc;
-    const bool gt = ok && key[i] > prefix, eq = ok && key[i] == prefix;
+    const bool gt = ok && (key[i] & pmask) > prefix, eq = ok && (key[i] & pmask) == prefix;
     const uint64_t bg = __ballot(gt), be = __ballot(eq);
     const uint64_t k64 = ((uint64_t)key[i] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
     if (gt) cand[seen_gt + __popcll(bg & below)] = k64;
