@@ -22,13 +22,15 @@
 //                 inputs would perturb scores by ~2^-9 relative and reorder
 //                 near-ties).
 //   topk_wave_kernel (Nc <= 2048) one wave per score row, rows independent:
-//                 the row's order-preserving score keys sit in registers; a
-//                 4-pass 8-bit radix select (LDS histogram per pass, a wave
-//                 suffix scan to find the digit) finds the k-th largest key;
-//                 the keys above it and the lowest-id keys equal to it are
-//                 compacted with ballots, and only those k are sorted (LDS
-//                 bitonic sort of 64-bit keys: score bits, then the
-//                 complemented cube id), descending.
+//                 the row's order-preserving score keys sit in registers; an
+//                 8-bit radix select of up to 4 passes (LDS histogram per
+//                 pass, a DPP prefix sum over the bins to find the digit;
+//                 it stops once every key on the resolved prefix is in the
+//                 top k) bounds the k-th largest key; the keys above it and
+//                 the lowest-id keys equal to it are compacted with ballots,
+//                 and only those k are sorted (64-bit keys: score bits, then
+//                 the complemented cube id), descending: by counting for up
+//                 to 128, by an LDS bitonic network beyond.
 //   topk_kernel   (larger rows) one workgroup per score row: a bitonic sort of
 //                 all of the row's 64-bit keys in LDS, descending; the first
 //                 topk ids are written out.
