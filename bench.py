@@ -188,8 +188,8 @@ def time_pipeline(case, vsa, torch, reps: int) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the VSA path here runs on a single MI355X; "
-              "multi-GPU runs are not part of this build (see the sharding notes).",
+        print("bench.py measures one GPU: the VSA path runs on a single MI355X; "
+              "multi-GPU runs are not supported (see the sharding notes).",
               file=sys.stderr)
         sys.exit(2)
     import torch
