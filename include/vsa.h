@@ -197,11 +197,12 @@ int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
 
 /* Bytes of device workspace vsa_fwd needs for these sizes: an fp16 copy of v
  * in the tiled layout (B * Nkv * 64 * NH * D * 2 bytes), then, per (b, h,
- * query cube) (B * NH * Nq of them), the list of the 32-token halves that
- * hold real tokens of its selected cubes ((2 * topk + 4) entries of two
- * uint32), its length (one int32), its dispatch rank (one int32) and the
- * rank's sort key (two int32), each part 256-byte aligned. Returns 0 for
- * invalid sizes. */
+ * query cube) (B * NH * Nq of them), the list of the 32-row tiles that hold
+ * real tokens of its selected cubes ((2 * topk + 4) entries of two uint32),
+ * its length (one int32), its dispatch rank (one int32) and the rank's sort
+ * key (two int32); then the largest |v| of every (v pre-pass workgroup, head)
+ * (B * Nkv * 8 * NH float32) and the per-(b, h) exponent of the fp16 copy
+ * (B * NH int32), each part 256-byte aligned. Returns 0 for invalid sizes. */
 size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
                                int32_t D, int32_t topk);
 
@@ -213,11 +214,14 @@ size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
  * where K, V are the rows 64j + u, u < vbs[j], of every j in
  * topk_idx[b, h, c, :]. q.k^T runs on bf16 inputs with fp32 accumulation;
  * the softmax is computed online in fp32 with a running row maximum
- * subtracted; the weights and V enter the P.V product as fp16 (V is exact in
- * fp16 for 2^-14 <= |v| <= 65504 and 0; larger magnitudes saturate to 65504,
- * smaller ones are truncated toward zero, an absolute error under 2^-24) with
- * fp32 accumulation; the output is rounded to bf16 (nearest even). A row with no
- * real key outputs 0.
+ * subtracted; the weights (rounded to fp16) and V enter the P.V product as
+ * fp16 with fp32 accumulation. V's fp16 copy is exact over the whole bf16
+ * range: a head (b, h) whose largest |v| lies outside [2^-4, 65504] is
+ * stored scaled by a power of two 2^-e (its largest |v| then in [2^14, 2^15),
+ * e in [-90, 113]) and its output multiplied back by 2^e; values below 2^-14
+ * (times 2^e) become fp16 subnormals, an absolute error under 2^-24 (times
+ * 2^e), at most 2^-20 of the head's largest |v|. The output is rounded to
+ * bf16 (nearest even). A row with no real key outputs 0.
  *   q         [B][Nq*64][NH][D] bf16, tiled order (padding rows are computed
  *             like real rows)
  *   k, v      [B][Nkv*64][NH][D] bf16, tiled order (padding values ignored)
@@ -229,7 +233,10 @@ size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
  *   workspace device buffer of >= vsa_fwd_workspace_bytes(B, Nq, Nkv, NH, D,
  *             topk) bytes, 256-byte aligned, not overlapping the tensors;
  *             contents on return are unspecified (it holds the fp16 copy of v
- *             and the half-tile lists)
+ *             and the tile lists). The workspace is an addition to the
+ *             operator contract's (q, k, v, topk_idx, vbs) -> out: PyTorch
+ *             (the caller) owns every allocation, so the fp16 copy of v and
+ *             the per-unit lists live in caller memory
  * In the dataset card's self-attention Nq = Nkv; other Nkv are accepted as long
  * as one batch of k spans less than 4 GiB, Nkv * 64 * NH * D * 2 < 2^32
  * (VSA_ERR_UNSUPPORTED beyond).

@@ -102,12 +102,14 @@ def test_fwd_validation():
     assert call(topk=9) == _lib.VSA_ERR_RANGE
     assert call(scale=float("nan")) == _lib.VSA_ERR_RANGE
     assert call(out=P + 2) == _lib.VSA_ERR_UNSUPPORTED
-    # fp16 v (8 cubes x 64 rows x 2 heads x 64 x 2 bytes), then the half-tile
-    # lists of the 16 (head, query cube) units ((2 * 3 + 4) entries x 8 bytes
+    # fp16 v (8 cubes x 64 rows x 2 heads x 64 x 2 bytes), then the tile
+    # lists of the 16 (head, query cube) units ((2 * 3 + 4) tiles x 8 bytes
     # each = 1280 bytes), then their lengths (16 int32 -> 256 after 256-byte
-    # rounding), then their dispatch ranks (16 int32 -> 256) and the ranks'
-    # sort keys (16 x 2 int32 -> 256)
-    need = 8 * 64 * 2 * 64 * 2 + 1280 + 256 + 256 + 256
+    # rounding), their dispatch ranks (16 int32 -> 256) and the ranks' sort
+    # keys (16 x 2 int32 -> 256), then the largest |v| of every (v pre-pass
+    # workgroup, head) (8 cubes x 8 workgroups x 2 heads float32 = 512) and
+    # the per-head exponent of the fp16 copy (2 int32 -> 256)
+    need = 8 * 64 * 2 * 64 * 2 + 1280 + 256 + 256 + 256 + 512 + 256
     assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 3) == need
     assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 0) == 0
     assert call(ws=None) == _lib.VSA_ERR_WORKSPACE

@@ -77,7 +77,8 @@ def _check(q, k, v, vbs, idx, valid, label, sm_scale=None):
     scale = 1 / math.sqrt(D) if sm_scale is None else sm_scale
     tol = _stat_tolerances(q64, k64, idx, valid, vbs, scale)
     tol_abs = tol + 8 * 2.0 ** -24 * np.abs(np.where(empty, 0, ref_lse))
-    d_lse = np.abs(np.where(empty, 0, lse - ref_lse))
+    # rows without keys hold -inf on both sides (checked above): mask before subtracting
+    d_lse = np.abs(np.where(empty, 0.0, lse) - np.where(empty, 0.0, ref_lse))
     d_mp = np.abs(np.where(empty, 0, mp / np.where(empty, 1, ref_mp) - 1))
     print(f"[{label}] max |d lse| {d_lse.max():.2e} (worst / bound {np.max(d_lse / np.maximum(tol_abs, 1e-30)):.3f});"
           f" max rel d max_prob {d_mp.max():.2e}", flush=True)

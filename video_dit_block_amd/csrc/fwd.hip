@@ -12,15 +12,17 @@
 //
 // Design for gfx950
 // -----------------
-// * Two pre-passes: (1) an fp16 copy of v (the PV product runs in fp16);
-//   (2) per (b, h, query cube) "unit", the selected cube ids sorted ascending
-//   and expanded into a list of 32-token half-tiles: half 0 of every cube with
-//   a real token, half 1 of every cube with more than 32. Each entry holds the
-//   half-tile's byte offset from the head's first key row and its real-row
-//   count, so the fine kernel builds a load descriptor with two scalar adds
-//   and never touches a half without real tokens. The result does not depend
-//   on the order of topk_idx; the ascending sweep makes the units resident on
-//   one XCD walk their head's key/value cubes in the same order.
+// * Pre-passes: (1) an fp16 copy of v (the PV product runs in fp16), exact
+//   over the bf16 range through a per-head power-of-two scale where a head's
+//   values leave fp16's normal range; (2) per (b, h, query cube) "unit", the
+//   selected cube ids sorted ascending and cut into quarters of at most 16
+//   real rows, consecutive quarters paired into 32-row tiles. Each quarter is
+//   its byte offset from the head's first key row plus its real-row count, so
+//   the fine kernel builds a load descriptor with two scalar operations and
+//   never spends a tile on padding rows except where a cube's real count is
+//   not a multiple of 16. The result does not depend on the order of
+//   topk_idx; the ascending sweep makes the units resident on one XCD walk
+//   their head's key/value cubes in the same order.
 // * One workgroup = one unit: 2 waves of 32 query rows, 4 workgroups per CU
 //   (2 waves per SIMD; 32 KiB of LDS each). Units are numbered head-major and
 //   remapped so each XCD walks a contiguous range. A third pre-pass orders
@@ -30,16 +32,16 @@
 //   sweeps close together and move at similar rates, so they keep sharing L2
 //   lines (measured on the Wan tensors: top-78 4.23 -> 3.99 ms; a lookup
 //   table at a 0.9 mass threshold 18.5 -> 14.1 ms).
-// * K and V half-tiles stream through LDS, each double-buffered, loaded
+// * K and V tiles stream through LDS, each double-buffered, loaded
 //   global -> LDS directly (buffer_load ... lds, two 1 KiB loads per M0
-//   write); every wave loads half of each tile. The buffer range of a load
-//   ends at the half's real rows, so padding rows land in LDS as zeros: pad
-//   values (even NaN) never reach an MFMA.
-// * Software pipeline inside each wave (step j = half-tile j):
-//     A(j): QK^T of half-tile j+1 (8 MFMAs) interleaved with the softmax
-//           exponentials, fp16 conversion and row sums of half-tile j;
-//     B(j): PV of half-tile j (8 MFMAs) interleaved with the mask and row
-//           max of half-tile j+1.
+//   write); wave w loads quarter w of each tile with its own descriptor. The
+//   buffer range of a load ends at the quarter's real rows, so padding rows
+//   land in LDS as zeros: pad values (even NaN) never reach an MFMA.
+// * Software pipeline inside each wave (step j = tile j):
+//     A(j): QK^T of tile j+1 (8 MFMAs) interleaved with the softmax
+//           exponentials, fp16 conversion and row sums of tile j;
+//     B(j): PV of tile j (8 MFMAs) interleaved with the mask and row
+//           max of tile j+1.
 //   Matrix and vector work of one wave thus overlap, and the second wave on
 //   the SIMD fills the remaining gaps. Loads keep 1.5 steps of lead: A(j)
 //   issues V(j+1), B(j) issues K(j+3).
@@ -47,7 +49,7 @@
 //   the A operand is a K row slice read from LDS, the B operand is the wave's
 //   Q held in registers for the whole loop. In the accumulator layout each
 //   lane then holds 16 scores of ONE query row (row l%32; the other 16 of the
-//   32-token half sit in lane l^32), so the row max and row sum need one
+//   32-token tile sit in lane l^32), so the row max and row sum need one
 //   cross-half swap (v_permlane32_swap) and the probabilities are already in
 //   the B-operand layout of O^T = V^T P^T: they go from accumulator to MFMA
 //   operand in registers. The contraction index of the PV product is
@@ -55,23 +57,26 @@
 //   of a summation index leaves the sum unchanged); the V^T operand comes
 //   from two transposing 8-byte LDS reads per lane (ds_read_b64_tr_b16) of
 //   row-major V.
-// * fp32 online softmax in the exp2 domain: p = exp2(s * c - m * c) with
+// * fp32 online softmax in the exp2 domain: p = exp2(s * c - m * c + 7) with
 //   c = sm_scale * log2 e (one FMA per score), reference max m, running sum
-//   l. The reference max is raised lazily: only when a half's row max
+//   l. The reference max is raised lazily: only when a tile's row max
 //   exceeds it by more than 2^8 (log2 units: 8) does the wave rescale O and l
-//   by exp2((m_old - m_new) c); otherwise p may reach 2^8, which fp32 and fp16
-//   hold exactly in range. Tokens past a half's real rows are set to -inf in
-//   registers before the max (partial halves only). O^T accumulates in fp32,
-//   each lane holding D/2 values of its own query row, so the rescale is a
-//   per-lane multiply.
+//   by exp2((m_old - m_new) c); otherwise p may reach 2^8 * 2^7, which fp32
+//   and fp16 hold in range. The constant 2^7 keeps weights down to 2^-21 of
+//   the reference max normal in fp16; it cancels in O / l. Tokens past a quarter's real rows are set to -inf
+//   in registers before the max (tiles with a partial quarter only). O^T
+//   accumulates in fp32, each lane holding D/2 values of its own query row,
+//   so the rescale is a per-lane multiply.
 // * Precision: QK^T is a bf16 MFMA with fp32 accumulation. The PV product
 //   runs as an fp16 MFMA (v_mfma_f32_32x32x16_f16): P is rounded to fp16 and
-//   V is converted to fp16 by the pre-pass. fp16 keeps 3 more
-//   significand bits than bf16, which matters for rows with few keys; V is
-//   converted exactly for 2^-14 <= |v| <= 65504 and 0 (there every bf16
-//   value is an fp16 value), saturates to 65504 above, and below 2^-14 (fp16
-//   subnormals) is truncated toward zero, an absolute error under 2^-24. O / l
-//   is rounded to bf16 (nearest even) and stored.
+//   V is converted to fp16 by the pre-pass. fp16 keeps 3 more significand
+//   bits than bf16, which matters for rows with few keys. Every bf16 value
+//   with 2^-14 <= |v| <= 65504 (and 0) is an fp16 value; heads whose largest
+//   |v| lies outside [2^-4, 65504] are converted scaled by a power of two
+//   2^-e_h, undone in the epilogue, so the copy is exact over the bf16 range
+//   up to fp16 subnormals (an absolute error under 2^-24 * 2^e_h, at most
+//   2^-20 of the head's largest |v|). O / l * 2^e_h is rounded to bf16
+//   (nearest even) and stored.
 #include <type_traits>
 
 #include "device.h"
@@ -85,7 +90,7 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kHalf = 32;  // tokens per half-tile
+constexpr int kTile = 32;  // tokens per tile (two quarters)
 
 template <int D>
 struct FwdShape {
@@ -93,11 +98,12 @@ struct FwdShape {
   static constexpr int kRowBytes = 2 * D;               // one (token, head) row
   static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
   static constexpr int kRowsPerKiB = 1024 / kRowBytes;  // rows one wave-wide load fills
-  static constexpr int kHalfBytes = kHalf * kRowBytes;  // one tensor of one half-tile
-  static constexpr int kLoads = kHalfBytes / 1024 / 2;  // loads per wave, tensor and half-tile
+  static constexpr int kTileBytes = kTile * kRowBytes;  // one tensor of one tile
+  static constexpr int kLoads = kTileBytes / 1024 / 2;  // loads per wave, tensor and tile
   static constexpr int kQSteps = D / 16;                // k-steps of the QK^T MFMAs
   static constexpr int kDBlocks = D / 32;               // 32-wide d blocks of O^T
   static_assert(kLoads % 2 == 0, "loads go in pairs");
+  static_assert(kLoads * kRowsPerKiB == 16, "each wave loads one 16-row quarter");
 };
 
 // XOR swizzles of the 16-byte chunk index inside an LDS row: chunk c of row r
@@ -125,6 +131,12 @@ template <> __device__ __forceinline__ int swz_v<64>(int r) {
 // raised when a tile's max exceeds it by more than this, so unnormalised
 // probabilities stay <= 2^8.
 constexpr float kRescaleThreshold = 8.0f;
+// Every probability is computed as 2^kPShift times its value relative to the
+// reference max: p in (0, 2^15] instead of (0, 2^8], still inside fp16's range
+// (65504), so that weights down to 2^-21 of the reference (not 2^-14) stay
+// normal fp16 numbers when P enters the P.V product. O and l carry the same
+// factor, which cancels in O / l; the row statistics remove it.
+constexpr float kPShift = 7.0f;
 constexpr int kBufferDword3 = 0x00020000;  // gfx9 raw buffer resource flags
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -186,68 +198,167 @@ template <int N>
 using IC = std::integral_constant<int, N>;
 
 // ---------------------------------------------------------------------------
-// V -> fp16 pre-pass. Writes an fp16 copy of v (same tiled BSHD layout) into
-// the workspace: real rows converted, padding rows zeroed. bf16 -> f32 is
-// exact (the bf16 bits are the upper half of an f32); f32 -> f16 with
-// truncation is exact for 2^-14 <= |v| <= 65504 and 0, since every such bf16
-// value is an fp16 value; it saturates to 65504 above, and below 2^-14 (fp16
-// subnormals) it loses at most 2^-24. HBM-bound: one read and one write of v.
+// V -> fp16 pre-pass, exact over the bf16 range. Every bf16 value whose
+// magnitude lies in [2^-14, 65504] (or is 0) is an fp16 value, so for the
+// usual inputs the conversion is a plain copy into the narrower format. A
+// head (b, h) whose largest |v| over its real rows is above 65504, or below
+// 2^-4, is instead stored scaled by 2^-e_h, e_h = floor(log2 max|v|) - 14
+// (clamped to [-90, 113]), which puts its largest magnitude in [2^14, 2^15);
+// multiplying by a power of two is exact, and the fine kernel multiplies the
+// head's output rows by 2^e_h. Three launches:
+//   v_to_fp16_kernel: real rows converted with e = 0, padding rows zeroed, and
+//     the largest |v| of every (workgroup, head) written to vmax;
+//   vscale_kernel:    per (b, h), e_h from the largest of those maxima;
+//   vfix_kernel:      the rows of heads with e_h != 0 converted again, scaled.
+// Only the first is HBM-bound (one read and one write of v); the other two
+// read a few hundred KiB and, for in-range heads, return at once.
+// Values below 2^-14 (times 2^e_h) become fp16 subnormals by truncation,
+// an absolute error under 2^-24 (times 2^e_h): at most 2^-20 of the head's
+// largest |v| when e_h = 0.
 constexpr int kCvtThreads = 256;
-constexpr int kCvtSplit = 8;   // workgroups per cube (8 slots each)
-constexpr int kCvtUnroll = 8;  // 16-byte loads in flight per lane
+constexpr int kCvtSplit = 8;    // workgroups per cube (8 slots each)
+constexpr int kCvtColBlk = 4;   // 64-lane column blocks per pass (x 2 rows = 8 loads in flight)
+constexpr int kVexpMin = -90, kVexpMax = 113;
+
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(const u32x4 w) {
+  // largest |x| of 8 bf16 values as fp32 bits (non-negative floats order as
+  // unsigned integers)
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = max(m, max((w[e] << 16) & 0x7FFF0000u, w[e] & 0x7FFF0000u));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t cvt2_fp16(uint32_t w, int e) {
+  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e == 0 ? lo : ldexpf(lo, -e),
+                                                                e == 0 ? hi : ldexpf(hi, -e)));
+}
 
 __device__ __forceinline__ u32x4 bf16x8_to_fp16x8(const u32x4 w) {
   u32x4 o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    o[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w[e] << 16),
-                                                                  __uint_as_float(w[e] & 0xFFFF0000u)));
+  for (int e = 0; e < 4; ++e) o[e] = cvt2_fp16(w[e], 0);
   return o;
 }
 
+// grid (Nkv * kCvtSplit, B); wave w converts rows 8 part + w and 8 part + 4 + w
+// of cube c. cph = 16-byte chunks per head (D / 8), cpr = per row (NH cph).
+// vmax[b][blockIdx.x][h] = largest |v| (fp32 bits) of the workgroup's real rows.
 __global__ __launch_bounds__(kCvtThreads) void v_to_fp16_kernel(
     const u32x4* __restrict__ v, u32x4* __restrict__ v16, const int32_t* __restrict__ vbs,
-    int Nkv, int cpr) {
+    uint32_t* __restrict__ vmax, int Nkv, int NH, int cph) {
+  __shared__ uint32_t red[kCvtThreads / 64][kCvtColBlk * 64];
   const int c = blockIdx.x / kCvtSplit, part = blockIdx.x % kCvtSplit, b = blockIdx.y;
   const int nv = min(max(vbs[c], 0), kCube);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-#pragma unroll 1
-  for (int r = 0; r < kCube / kCvtSplit / 4; ++r) {
-    const int u = part * (kCube / kCvtSplit) + r * 4 + wave;
-    const size_t row = ((size_t)b * Nkv + c) * kCube + u;
-    const u32x4* __restrict__ src = v + row * cpr;
-    u32x4* __restrict__ dst = v16 + row * cpr;
-    if (u < nv) {
-      int col = lane;
-      for (; col + 64 * (kCvtUnroll - 1) < cpr; col += 64 * kCvtUnroll) {
-        u32x4 w[kCvtUnroll];
+  const int cpr = NH * cph;
+  const int u0 = part * (kCube / kCvtSplit) + wave, u1 = u0 + 4;
+  const size_t row0 = ((size_t)b * Nkv + c) * kCube + u0;
+  const u32x4* __restrict__ src0 = v + row0 * cpr;
+  const u32x4* __restrict__ src1 = src0 + (size_t)4 * cpr;
+  u32x4* __restrict__ dst0 = v16 + row0 * cpr;
+  u32x4* __restrict__ dst1 = dst0 + (size_t)4 * cpr;
+  uint32_t* __restrict__ vm = vmax + ((size_t)b * gridDim.x + blockIdx.x) * NH;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int c0 = 0; c0 < cpr; c0 += 64 * kCvtColBlk) {
+    u32x4 w0[kCvtColBlk], w1[kCvtColBlk];
 #pragma unroll
-        for (int i = 0; i < kCvtUnroll; ++i) w[i] = __builtin_nontemporal_load(src + col + 64 * i);
+    for (int i = 0; i < kCvtColBlk; ++i) {
+      const int col = c0 + 64 * i + lane;
+      w0[i] = (col < cpr && u0 < nv) ? __builtin_nontemporal_load(src0 + col) : z;
+      w1[i] = (col < cpr && u1 < nv) ? __builtin_nontemporal_load(src1 + col) : z;
+    }
 #pragma unroll
-        for (int i = 0; i < kCvtUnroll; ++i) dst[col + 64 * i] = bf16x8_to_fp16x8(w[i]);
+    for (int i = 0; i < kCvtColBlk; ++i) {
+      const int col = c0 + 64 * i + lane;
+      if (col < cpr) {
+        dst0[col] = bf16x8_to_fp16x8(w0[i]);  // zeros for padding rows
+        dst1[col] = bf16x8_to_fp16x8(w1[i]);
       }
-      for (; col < cpr; col += 64) dst[col] = bf16x8_to_fp16x8(__builtin_nontemporal_load(src + col));
-    } else {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      for (int col = lane; col < cpr; col += 64) dst[col] = z;
+      // largest |v| of the head's chunks in these two rows: reduce over the
+      // cph lanes of each head (heads start at multiples of cph lanes)
+      uint32_t m = max(bf16x8_absmax_bits(w0[i]), bf16x8_absmax_bits(w1[i]));
+      for (int o = 1; o < cph; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+      red[wave][64 * i + lane] = m;
+    }
+    __syncthreads();
+    // one lane per head of this pass combines the four waves
+    const int heads = min(kCvtColBlk * 64, cpr - c0) / cph;
+    if (wave == 0 && lane < heads) {
+      const int t = lane * cph;
+      const uint32_t m = max(max(red[0][t], red[1][t]), max(red[2][t], red[3][t]));
+      vm[c0 / cph + lane] = m;
+    }
+    __syncthreads();
+  }
+}
+
+// grid (NH, B), 256 threads: e_h from the largest of the head's workgroup maxima.
+__global__ __launch_bounds__(256) void vscale_kernel(const uint32_t* __restrict__ vmax,
+                                                     int32_t* __restrict__ vexp, int n_wg, int NH) {
+  __shared__ uint32_t red[4];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const uint32_t* __restrict__ vm = vmax + (size_t)b * n_wg * NH + h;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n_wg; i += 256) m = max(m, vm[(size_t)i * NH]);
+  for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float M = __uint_as_float(m);
+    int e = 0;
+    if (M > 65504.0f || (M > 0.0f && M < 0.0625f))
+      e = min(max(ilogbf(M) - 14, kVexpMin), kVexpMax);
+    vexp[(size_t)b * NH + h] = e;
+  }
+}
+
+// grid (Nkv * kCvtSplit, B): the real rows of every head with e_h != 0,
+// converted again with the scale 2^-e_h (padding rows are zero already).
+__global__ __launch_bounds__(kCvtThreads) void vfix_kernel(
+    const uint32_t* __restrict__ v, uint32_t* __restrict__ v16, const int32_t* __restrict__ vbs,
+    const int32_t* __restrict__ vexp, int Nkv, int NH, int D) {
+  const int c = blockIdx.x / kCvtSplit, part = blockIdx.x % kCvtSplit, b = blockIdx.y;
+  const int nv = min(max(vbs[c], 0), kCube);
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wpr = NH * D / 2;  // 32-bit words (bf16 pairs) per row
+  for (int h = 0; h < NH; ++h) {
+    const int e = vexp[(size_t)b * NH + h];
+    if (e == 0) continue;
+    for (int r = 0; r < kCube / kCvtSplit / 4; ++r) {
+      const int u = part * (kCube / kCvtSplit) + r * 4 + wave;
+      if (u >= nv) continue;
+      const size_t row = ((size_t)b * Nkv + c) * kCube + u;
+      for (int j = lane; j < D / 2; j += 64) {
+        const size_t i = row * wpr + (size_t)h * (D / 2) + j;
+        v16[i] = cvt2_fp16(v[i], e);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Half-tile list pre-pass: one wave per unit (b, h, query cube). The unit's
+// Tile list pre-pass: one wave per unit (b, h, query cube). The unit's
 // selected ids (the first valid[unit] entries of its index row, or all of
 // them; clamped into range: a violated precondition gives unspecified values,
-// never an out-of-bounds access) are sorted ascending and expanded into
-// 32-token half-tiles: half 0 of every cube with a real token, half 1 of
-// every cube with more than 32. Entry = (byte offset of the half from the
-// head's first key row, real rows of the half), two uint32; kListPad (0, 0)
-// entries follow the last one. Rows with topk > kListSortCap keep the given
-// order.
+// never an out-of-bounds access) are sorted ascending and every cube with
+// real tokens is cut into quarters of at most 16 rows (ceil(vbs / 16) of
+// them: rows 0-15, 16-31, ...). Consecutive quarters pair up into 32-row
+// tiles, the unit of the fine kernel's loop: a cube of 16 or 8 real tokens
+// shares its tile with the next cube's first quarter instead of leaving half
+// a tile of padding (at the Wan shape this removes about 5% of the tiles).
+// A quarter is one uint32: its byte offset from the head's first key row
+// (a multiple of 16 row strides, so of 2048) OR its real-row count (1..16).
+// Tile t = quarters 2t and 2t+1; an odd last quarter is paired with 0 (no
+// rows), and kListPad all-zero tiles follow the last one. Rows with
+// topk > kListSortCap keep the given order.
 constexpr int kListSortCap = 1024;
 constexpr int kListPad = 4;
+constexpr int kQuarter = 16;  // rows per quarter
 
-__global__ __launch_bounds__(64) void halves_kernel(
+__global__ __launch_bounds__(64) void tiles_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ valid,
     const int32_t* __restrict__ vbs, uint32_t* __restrict__ list, int32_t* __restrict__ counts,
     int Nkv, int row_len, int stride, uint32_t rs2) {
@@ -280,7 +391,7 @@ __global__ __launch_bounds__(64) void halves_kernel(
     __syncthreads();
   }
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  int base = 0;
+  int base = 0;  // quarters written so far
   for (int c0 = 0; c0 < topk; c0 += 64) {
     const int i = c0 + lane;
     int id = 0, nv = 0;
@@ -288,28 +399,29 @@ __global__ __launch_bounds__(64) void halves_kernel(
       id = sorted ? keys[i] : id_at(i);
       nv = min(max(vbs[id], 0), kCube);
     }
-    const uint64_t b1 = __builtin_amdgcn_ballot_w64(nv > 0);
-    const uint64_t b2 = __builtin_amdgcn_ballot_w64(nv > kHalf);
-    const int pos = base + __builtin_popcountll(b1 & below) + __builtin_popcountll(b2 & below);
+    const int nq = (nv + kQuarter - 1) / kQuarter;  // 0..4
+    int pos = base, tot = 0;
+#pragma unroll
+    for (int k = 1; k <= kCube / kQuarter; ++k) {
+      const uint64_t bk = __builtin_amdgcn_ballot_w64(nq >= k);
+      pos += __builtin_popcountll(bk & below);
+      tot += __builtin_popcountll(bk);
+    }
     const uint32_t off0 = (uint32_t)id * (uint32_t)kCube * rs2;
-    if (nv > 0) {
-      out[2 * pos] = off0;
-      out[2 * pos + 1] = (uint32_t)min(nv, kHalf);
-    }
-    if (nv > kHalf) {
-      out[2 * pos + 2] = off0 + (uint32_t)kHalf * rs2;
-      out[2 * pos + 3] = (uint32_t)(nv - kHalf);
-    }
-    base += __builtin_popcountll(b1) + __builtin_popcountll(b2);
+    for (int k = 0; k < nq; ++k)
+      out[pos + k] = (off0 + (uint32_t)(kQuarter * k) * rs2) | (uint32_t)min(nv - kQuarter * k, kQuarter);
+    base += tot;
   }
-  if (lane < 2 * kListPad) out[2 * base + lane] = 0u;
-  if (lane == 0) counts[unit] = base;
+  const int n_tiles = (base + 1) / 2;
+  if (lane == 0 && (base & 1)) out[base] = 0u;
+  if (lane < 2 * kListPad) out[2 * n_tiles + lane] = 0u;
+  if (lane == 0) counts[unit] = n_tiles;
 }
 
 // Dispatch order inside each (b, h): query cubes by descending count of
 // selected cubes, then by ascending smallest selected id, then by cube id.
 // Units that run side by side then sweep the ascending key ids from nearby
-// starting points at similar rates, so their half-tile loads keep hitting the
+// starting points at similar rates, so their tile loads keep hitting the
 // same L2 lines, and with per-row counts the longest units start first.
 // Two passes: order_key_kernel writes one packed key per unit, a lane quad
 // per unit; order_rank_kernel ranks each head's keys, grid (B*NH,
@@ -360,11 +472,12 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v16, const uint32_t* __restrict__ list,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ order,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ max_prob, int Nq,
-    int Nkv, int NH, int list_stride, float scale_log2, int n_units) {
+    const int32_t* __restrict__ vexp, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ max_prob, int Nq, int Nkv, int NH, int list_stride, float scale_log2,
+    int n_units) {
   using S = FwdShape<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][S::kHalfBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][S::kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][S::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][S::kTileBytes];
 
   // XCD x runs a contiguous range of (b, h, rank); within a (b, h) the query
   // cube of a rank is the rank itself, or order[] for per-row counts
@@ -390,8 +503,8 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   }
   uint16_t* const orow = out + qrow * row_stride + (size_t)h * D;
 
-  // ---- the unit's half-tiles; reads past the list (i >= n) see the (0, 0)
-  // padding entries (i < n + kListPad)
+  // ---- the unit's tiles (two quarters each); reads past the list (i >= n)
+  // see the all-zero padding tiles (i < n + kListPad)
   const uint32_t* __restrict__ lst = list + (size_t)unit * list_stride * 2;
   const int n = __builtin_amdgcn_readfirstlane(counts[unit]);
   auto ent = [&](int i) __attribute__((always_inline)) -> u32x2 {
@@ -412,42 +525,48 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     return;
   }
 
-  // ---- loads: wave w fills KiB [L w, L w + L) of every half-tile buffer
-  // (L = kLoads), lane L' writing bytes [16 L', 16 L' + 16) of a KiB; the
-  // lane fetches the global chunk that the swizzle places in that slot.
-  // Byte offsets stay below 2^32 (host-checked).
+  // ---- loads: wave w fills KiB [L w, L w + L) of every tile buffer
+  // (L = kLoads), i.e. tile rows [16 w, 16 w + 16): quarter w of the tile;
+  // lane L' writes bytes [16 L', 16 L' + 16) of a KiB and fetches the global
+  // chunk that the swizzle places in that slot. Byte offsets stay below 2^32
+  // (host-checked).
   constexpr int L = S::kLoads;
   const uint32_t rs2 = (uint32_t)NH * D * 2u;
   uint32_t koff[L], voff[L];
 #pragma unroll
   for (int m = 0; m < L; ++m) {
+    // LDS row of the tile, and its row inside this wave's quarter (the
+    // descriptor's base is the quarter's first row)
     const int row = (wave * L + m) * S::kRowsPerKiB + lane / S::kChunks;
+    const int qrow = row - kQuarter * wave;
     const int slot = lane % S::kChunks;
-    koff[m] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_k<D>(row)) - 1024u * (m & 1);
-    voff[m] = (uint32_t)row * rs2 + 16u * (uint32_t)(slot ^ swz_v<D>(row)) - 1024u * (m & 1);
+    koff[m] = (uint32_t)qrow * rs2 + 16u * (uint32_t)(slot ^ swz_k<D>(row)) - 1024u * (m & 1);
+    voff[m] = (uint32_t)qrow * rs2 + 16u * (uint32_t)(slot ^ swz_v<D>(row)) - 1024u * (m & 1);
   }
   const uint32_t lds_wave = (uint32_t)(wave * L) * 1024u;
   const size_t kv_head = (size_t)b * Nkv * kCube * row_stride + (size_t)h * D;
   const uint64_t kbase = reinterpret_cast<uint64_t>(k + kv_head);
   const uint64_t vbase = reinterpret_cast<uint64_t>(v16 + kv_head);
-  // gfx9 raw buffer descriptor of one half-tile: base + offset, range = its
-  // real rows (the loads of padding rows and of (0, 0) entries return zeros)
+  // gfx9 raw buffer descriptor of this wave's quarter of a tile: base +
+  // offset, range = its real rows (the loads of padding rows and of empty
+  // quarters return zeros)
   auto mk_rsrc = [&](uint64_t base, const u32x2& e) __attribute__((always_inline)) -> int32x4_t {
-    const uint64_t a = base + e[0];
+    const uint32_t qw = wave ? e[1] : e[0];
+    const uint64_t a = base + (qw & ~31u);
     int32x4_t r;
     r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
     r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xFFFFu));
-    r[2] = __builtin_amdgcn_readfirstlane((int)(e[1] * rs2));
+    r[2] = __builtin_amdgcn_readfirstlane((int)((qw & 31u) * rs2));
     r[3] = kBufferDword3;
     return r;
   };
   const uint32_t kb0 = lds_address(kbuf), vb0 = lds_address(vbuf);
-  // load pair p (0 <= p < L / 2) of a half-tile into buffer `buf`
+  // load pair p (0 <= p < L / 2) of a tile into buffer `buf`
   auto dma_k = [&](const int32x4_t& r, int buf, int p) __attribute__((always_inline)) {
-    dma16x2(r, koff[2 * p], koff[2 * p + 1], kb0 + (uint32_t)buf * S::kHalfBytes + lds_wave + 2048u * p);
+    dma16x2(r, koff[2 * p], koff[2 * p + 1], kb0 + (uint32_t)buf * S::kTileBytes + lds_wave + 2048u * p);
   };
   auto dma_v = [&](const int32x4_t& r, int buf, int p) __attribute__((always_inline)) {
-    dma16x2(r, voff[2 * p], voff[2 * p + 1], vb0 + (uint32_t)buf * S::kHalfBytes + lds_wave + 2048u * p);
+    dma16x2(r, voff[2 * p], voff[2 * p + 1], vb0 + (uint32_t)buf * S::kTileBytes + lds_wave + 2048u * p);
   };
 
   // ---- per-lane LDS read addresses in buffer 0 (buffer 1 is a constant
@@ -488,22 +607,22 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   const floatx16 zero16 = {};
   const halfx2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  // S^T = K Q^T for the half-tile in K buffer kbi; V load pairs ride along
+  // S^T = K Q^T for the tile in K buffer kbi; V load pairs ride along
   auto qk = [&](int kbi, floatx16& s, const int32x4_t& vr, int vbi) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < S::kQSteps; ++st) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl[st] + kbi * S::kHalfBytes);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl[st] + kbi * S::kTileBytes);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], st == 0 ? zero16 : s, 0, 0, 0);
       if (vbi >= 0 && st % 2 == 1 && st / 2 < L / 2) dma_v(vr, vbi, st / 2);
     }
   };
-  // O^T += V^T P^T for the half-tile in V buffer vbi; K load pairs ride along
+  // O^T += V^T P^T for the tile in V buffer vbi; K load pairs ride along
   auto pv = [&](int vbi, const halfx8 (&pb)[2], const int32x4_t& kr, int kbi) __attribute__((always_inline)) {
     constexpr int NSTEP = 2 * S::kDBlocks;  // (kk, db)
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       const int kk = st / S::kDBlocks, db = st % S::kDBlocks;
-      const uint8_t* p0 = vl[db] + vbi * S::kHalfBytes + kk * 16 * S::kRowBytes;
+      const uint8_t* p0 = vl[db] + vbi * S::kTileBytes + kk * 16 * S::kRowBytes;
       const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p0)));
       const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_ptr)(p0 + 8 * S::kRowBytes)));
       const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -511,17 +630,20 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
       if (kbi >= 0 && st % 2 == 1 && st / 2 < L / 2) dma_k(kr, kbi, st / 2);
     }
   };
-  // tokens >= the half's real rows set to -inf (partial halves only; the asm
-  // keeps the compiler from flattening the branch into selects that every
-  // half would execute), row max, lazy raise of the reference max
-  // (wave-uniform decision)
-  auto mask_max = [&](uint32_t nvh, floatx16& s) __attribute__((always_inline)) {
-    if (nvh < (uint32_t)kHalf) {
+  // tokens past the real rows of their quarter set to -inf (tiles with a
+  // partial quarter only; the asm keeps the compiler from flattening the
+  // branch into selects that every tile would execute), row max, lazy raise
+  // of the reference max (wave-uniform decision). Accumulator entry r holds
+  // token 8 (r / 4) + 4 g + r % 4: entries 0-7 lie in quarter 0 (tokens
+  // 0-15), entries 8-15 in quarter 1.
+  auto mask_max = [&](const u32x2& e, floatx16& s) __attribute__((always_inline)) {
+    const uint32_t na = e[0] & 31u, nb = e[1] & 31u;
+    if ((na & nb) < (uint32_t)kQuarter) {
       asm volatile("");
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t tok = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (tok >= nvh) s[r] = kNegInf;
+        if (r < 8 ? tok >= na : tok - kQuarter >= nb) s[r] = kNegInf;
       }
     }
     float mx = kNegInf;
@@ -540,9 +662,9 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   };
   // P in fp16 (round to nearest even) and the row sums of the same rounded
   // values (v_dot2_f32_f16 against 1.0). Every row has a finite m_ref here:
-  // the first half-tile of a unit holds at least one real token.
+  // the first tile of a unit holds at least one real token.
   auto exp_sum = [&](const floatx16& s, halfx8 (&pb)[2]) __attribute__((always_inline)) {
-    const float mc = m_ref * scale_log2;
+    const float mc = m_ref * scale_log2 - kPShift;
     float rs = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -589,7 +711,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     wait_vmcnt<2 * L>();  // K(0): K(1), V(0) may be in flight
     __syncthreads();
     qk(0, sA, r0, -1);
-    mask_max(e0[1], sA);
+    mask_max(e0, sA);
     need_rescale = false;  // O and l are still zero
   }
 
@@ -622,7 +744,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     wait_vmcnt<2 * L>();  // V(j)
     __syncthreads();
     pv(P, pb, mk_rsrc(kbase, e_n3), P ^ 1);
-    mask_max(e_n1[1], sn);
+    mask_max(e_n1, sn);
     e_n1 = e_n2;
     e_n2 = e_n3;
   };
@@ -652,17 +774,19 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
       pv(0, pb, none, -1);
   }
 
-  // ---- per-row statistics. l_run sums exp2((s - m_ref) c), so the natural
-  // log-sum-exp of the scaled scores is (m_ref c + log2 l_run) ln 2, and the
-  // largest softmax weight is 1 / sum exp2((s - m_row) c) =
-  // exp2((m_row - m_ref) c) / l_run.
+  // ---- per-row statistics. l_run sums exp2((s - m_ref) c + kPShift), so the
+  // natural log-sum-exp of the scaled scores is (m_ref c - kPShift +
+  // log2 l_run) ln 2, and the largest softmax weight is
+  // 1 / sum exp2((s - m_row) c) = exp2((m_row - m_ref) c + kPShift) / l_run.
   if (g == 0 && lse != nullptr)
-    lse[srow] = (m_ref * scale_log2 + __log2f(l_run)) * 0.69314718055994531f;
+    lse[srow] = (m_ref * scale_log2 - kPShift + __log2f(l_run)) * 0.69314718055994531f;
   if (g == 0 && max_prob != nullptr)
-    max_prob[srow] = __builtin_amdgcn_exp2f((m_row - m_ref) * scale_log2) / l_run;
+    max_prob[srow] = __builtin_amdgcn_exp2f((m_row - m_ref) * scale_log2 + kPShift) / l_run;
 
-  // ---- epilogue: lane holds O^T[d][row] for d = 32 db + 8 (r/4) + 4 g + r%4
-  const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  // ---- epilogue: lane holds O^T[d][row] for d = 32 db + 8 (r/4) + 4 g + r%4;
+  // V entered the product scaled by 2^-e_h (0 for heads in fp16's range)
+  const int ve = vexp == nullptr ? 0 : vexp[bh];
+  const float inv_l = l_run > 0.0f ? ldexpf(1.0f / l_run, ve) : 0.0f;
 #pragma unroll
   for (int db = 0; db < S::kDBlocks; ++db)
 #pragma unroll
@@ -678,14 +802,17 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk) {
   auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
   FwdWorkspace w;
-  w.list_stride = 2 * topk + kListPad;  // entries per unit, 8 bytes each
+  // tiles per unit: at most 4 quarters per cube, two per tile
+  w.list_stride = 2 * topk + kListPad;  // tiles per unit, 8 bytes each
   const size_t units = (size_t)B * NH * Nq;
   w.v16_off = 0;
   w.list_off = up((size_t)B * Nkv * kCube * NH * D * 2);
   w.count_off = w.list_off + up(units * w.list_stride * 8);
   w.order_off = w.count_off + up(units * 4);
   w.key_off = w.order_off + up(units * 4);
-  w.total = w.key_off + up(units * 8);
+  w.vmax_off = w.key_off + up(units * 8);
+  w.vexp_off = w.vmax_off + up((size_t)B * Nkv * kCvtSplit * NH * 4);
+  w.total = w.vexp_off + up((size_t)B * NH * 4);
   return w;
 }
 
@@ -699,13 +826,23 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   uint16_t* v16 = reinterpret_cast<uint16_t*>(ws + w.v16_off);
   uint32_t* list = reinterpret_cast<uint32_t*>(ws + w.list_off);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + w.count_off);
+  uint32_t* vmax = reinterpret_cast<uint32_t*>(ws + w.vmax_off);
+  int32_t* vexp = reinterpret_cast<int32_t*>(ws + w.vexp_off);
   int32_t* order = nullptr;
-  const int cpr = NH * D / 8;
   const int n_units = B * NH * Nq;
   hipLaunchKernelGGL(v_to_fp16_kernel, dim3(Nkv * kCvtSplit, B), dim3(kCvtThreads), 0, stream,
-                     reinterpret_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(v16), vbs, Nkv,
-                     cpr);
+                     reinterpret_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(v16), vbs, vmax,
+                     Nkv, NH, D / 8);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vscale_kernel, dim3(NH, B), dim3(256), 0, stream, vmax, vexp,
+                     Nkv * kCvtSplit, NH);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vfix_kernel, dim3(Nkv * kCvtSplit, B), dim3(kCvtThreads), 0, stream,
+                     reinterpret_cast<const uint32_t*>(v), reinterpret_cast<uint32_t*>(v16), vbs,
+                     vexp, Nkv, NH, D);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   // The order pass runs ahead of the list pass: launched right before the
   // fine kernel it cost that kernel about 1 ms at 312 cubes per row
@@ -724,18 +861,18 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(halves_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, valid, vbs,
+  hipLaunchKernelGGL(tiles_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, valid, vbs,
                      list, counts, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   if (D == 128)
     hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_units), dim3(FwdShape<128>::kThreads), 0, stream,
-                       q, k, v16, list, counts, order, out, lse, max_prob, Nq, Nkv, NH,
+                       q, k, v16, list, counts, order, vexp, out, lse, max_prob, Nq, Nkv, NH,
                        w.list_stride, scale_log2, n_units);
   else
     hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_units), dim3(FwdShape<64>::kThreads), 0, stream,
-                       q, k, v16, list, counts, order, out, lse, max_prob, Nq, Nkv, NH,
+                       q, k, v16, list, counts, order, vexp, out, lse, max_prob, Nq, Nkv, NH,
                        w.list_stride, scale_log2, n_units);
   return hipGetLastError();
 }

@@ -64,10 +64,11 @@ hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          void* workspace, hipStream_t stream);
 
 // Workspace carve-up of vsa_fwd: an fp16 copy of v in the tiled layout, the
-// half-tile lists of the units ([B*NH*Nq][list_stride] pairs of uint32), their
-// lengths, the dispatch order and its sort keys.
+// tile lists of the units ([B*NH*Nq][list_stride] pairs of uint32 quarters),
+// their lengths, the dispatch order and its sort keys, the per-(workgroup,
+// head) maxima of |v| and the per-(b, h) exponent of v's fp16 copy.
 struct FwdWorkspace {
-  size_t v16_off, list_off, count_off, order_off, key_off, total;
+  size_t v16_off, list_off, count_off, order_off, key_off, vmax_off, vexp_off, total;
   int list_stride;
 };
 FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk);
