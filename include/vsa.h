@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 4
+#define VSA_ABI_VERSION 5
 #define VSA_CUBE 64
 
 typedef uint16_t vsa_bf16_t; /* raw bf16 bits */
@@ -167,6 +167,27 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                    const int32_t* vbs, int32_t B, int32_t Nc, int32_t NH,
                    int32_t D, int32_t topk, int32_t* topk_idx, void* workspace,
                    size_t workspace_bytes, vsa_stream_t stream);
+
+/* vsa_select without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Computes exactly what vsa_select computes, with the
+ * same kernels, into topk_idx; its scratch (pooled q and k, the cube scores)
+ * is a device array of vsa_select_noalloc_max_bytes() = 64 MiB inside the
+ * library, one per GPU, held from its first use on that GPU until the process
+ * ends. The (batch, head) pairs are processed in chunks of as many heads as
+ * fit (30 at the Wan shape, 4 at Nc = 1920), all on `stream`. Nothing in the
+ * scratch needs clearing: every byte a call reads it has written first.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * behind: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race and give undefined ids; order
+ * them on one stream. No device memory is allocated or freed. Errors: as for
+ * vsa_select, without VSA_ERR_WORKSPACE; VSA_ERR_UNSUPPORTED also when one
+ * head's workspace (vsa_select_workspace_bytes(1, 1, Nc, D)) exceeds the
+ * scratch (Nc above about 4000 at D = 128). */
+size_t vsa_select_noalloc_max_bytes(void);
+int32_t vsa_select_noalloc(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                           const int32_t* vbs, int32_t B, int32_t Nc, int32_t NH, int32_t D,
+                           int32_t topk, int32_t* topk_idx, vsa_stream_t stream);
 
 /* Coarse selector with a cumulative-mass threshold (Optimizing block-sparse
  * INT8 attention and multi-expert step caching for Wan 2.2, section

@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.vsa_abi_version() == 4
+    assert lib.vsa_abi_version() == 5
     for s, name in [(0, "VSA_OK"), (1, "VSA_ERR_NULL"), (2, "VSA_ERR_SHAPE"),
                     (3, "VSA_ERR_UNSUPPORTED"), (4, "VSA_ERR_RANGE"), (5, "VSA_ERR_WORKSPACE"),
                     (6, "VSA_ERR_HIP")]:
@@ -117,6 +117,24 @@ def test_fwd_validation():
     # one batch of k must span < 4 GiB: Nkv * 64 * NH * D * 2 = Nkv * 16384 here
     assert call(Nkv=1 << 18, topk=3) == _lib.VSA_ERR_UNSUPPORTED
     assert call(ws=P + 128) == _lib.VSA_ERR_WORKSPACE
+
+
+def test_select_noalloc_validation():
+    """The allocation-free selector rejects bad arguments on the host, and a
+    shape whose single head needs more than its static scratch."""
+    lib = _lib.load()
+    cap = lib.vsa_select_noalloc_max_bytes()
+    assert cap == 64 << 20
+    args = lambda topk, nc=8, d=64, q=P: (q, P, P, 1, nc, 2, d, topk, P, None)
+    assert lib.vsa_select_noalloc(*args(3, q=None)) == _lib.VSA_ERR_NULL
+    assert lib.vsa_select_noalloc(*args(0)) == _lib.VSA_ERR_RANGE
+    assert lib.vsa_select_noalloc(*args(9)) == _lib.VSA_ERR_RANGE
+    assert lib.vsa_select_noalloc(*args(3, d=80)) == _lib.VSA_ERR_UNSUPPORTED
+    assert lib.vsa_select_noalloc(*args(3, nc=8193)) == _lib.VSA_ERR_UNSUPPORTED
+    # one head of 4096 cubes at D = 128: 4096^2 x 4 bytes of scores alone
+    assert lib.vsa_select_workspace_bytes(1, 1, 4096, 128) > cap
+    assert lib.vsa_select_noalloc(*args(4, nc=4096, d=128)) == _lib.VSA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.vsa_last_error()
 
 
 def test_coarse_and_combine_validation():

@@ -5,4 +5,5 @@ the kernels' sources (csrc/), the build script and a thin torch/ctypes
 binding."""
 from .ops import (coarse, coarse_workspace_bytes, cube_order, default_scale, fwd,  # noqa: F401
                   fwd_lut, fwd_workspace_bytes, gate_combine, mask_to_lut, num_cubes, select,
-                  select_cdf, select_workspace_bytes, tile, untile, validate_topk, vbs_host)
+                  select_cdf, select_noalloc, select_noalloc_max_bytes, select_workspace_bytes,
+                  tile, untile, validate_topk, vbs_host)

@@ -45,6 +45,9 @@ SIGNATURES = {
     "vsa_select_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int]),
     "vsa_select": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                             _sz, _vp]),
+    "vsa_select_noalloc_max_bytes": (_sz, []),
+    "vsa_select_noalloc": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp,
+                                    _vp]),
     "vsa_select_cdf": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
     "vsa_fwd_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "vsa.h"
 
@@ -66,6 +68,38 @@ int32_t check_grid(int32_t T, int32_t H, int32_t W, int64_t* nc) {
   *nc = num_cubes64(T, H, W);
   if (*nc < 0) return fail(VSA_ERR_SHAPE, "grid %dx%dx%d must be positive", T, H, W);
   if (*nc * 4 > kMaxGridX) return fail(VSA_ERR_SHAPE, "too many cubes: %lld", (long long)*nc);
+  return VSA_OK;
+}
+
+// Scratch of vsa_select_noalloc: the selector's workspace (pooled q and k,
+// the cube scores) for as many (batch, head) pairs as fit, in a file-scope
+// device array. Every GPU the library runs on holds its own copy of it until
+// the process ends. In host code `scratch` names a host-side stand-in, not
+// device memory: kernels and copies receive the per-device address that
+// hipGetSymbolAddress returns, taken once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int32_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(VSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(VSA_ERR_UNSUPPORTED, "device %d above the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(VSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
   return VSA_OK;
 }
 
@@ -241,6 +275,48 @@ int32_t vsa_select(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                                      nullptr, 0.0f, 0.0f, workspace,
                                      static_cast<hipStream_t>(stream)),
                   "select");
+}
+
+size_t vsa_select_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int32_t vsa_select_noalloc(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
+                           const int32_t* vbs, int32_t B, int32_t Nc, int32_t NH, int32_t D,
+                           int32_t topk, int32_t* topk_idx, vsa_stream_t stream) {
+  if (q_tiled == nullptr || k_tiled == nullptr || vbs == nullptr || topk_idx == nullptr)
+    return fail(VSA_ERR_NULL, "q_tiled, k_tiled, vbs or topk_idx is NULL");
+  int32_t s = check_bhd(B, NH, D);
+  if (s != VSA_OK) return s;
+  if (Nc <= 0) return fail(VSA_ERR_SHAPE, "Nc=%d must be positive", Nc);
+  if (Nc > VSA_MAX_CUBES)
+    return fail(VSA_ERR_UNSUPPORTED, "Nc=%d exceeds VSA_MAX_CUBES=%d", Nc, VSA_MAX_CUBES);
+  if (topk < 1 || topk > Nc) return fail(VSA_ERR_RANGE, "topk=%d outside [1, %d]", topk, Nc);
+  if (!aligned16(q_tiled) || !aligned16(k_tiled))
+    return fail(VSA_ERR_UNSUPPORTED, "q_tiled and k_tiled must be 16-byte aligned");
+  // heads per chunk: the most whose workspace fits the scratch
+  const size_t one = vsa::select_workspace(1, 1, Nc, D).total;
+  if (one > kNoAllocScratchBytes)
+    return fail(VSA_ERR_UNSUPPORTED,
+                "one head of Nc=%d cubes needs %zu bytes of scratch, above the %zu of "
+                "vsa_select_noalloc (use vsa_select with a workspace)",
+                Nc, one, kNoAllocScratchBytes);
+  int32_t chunk = (int32_t)(kNoAllocScratchBytes / one);
+  if (chunk > NH) chunk = NH;
+  while (chunk > 1 && vsa::select_workspace(1, chunk, Nc, D).total > kNoAllocScratchBytes) --chunk;
+  if ((s = check_device()) != VSA_OK) return s;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != VSA_OK) return s;
+  const size_t row = (size_t)NH * D;  // elements per tiled token row
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t h0 = 0; h0 < NH; h0 += chunk) {
+      const int32_t nh = NH - h0 < chunk ? NH - h0 : chunk;
+      const size_t off = (size_t)b * Nc * 64 * row + (size_t)h0 * D;
+      int32_t* idx = topk_idx + ((size_t)b * NH + h0) * Nc * topk;
+      const hipError_t e = vsa::launch_select(q_tiled + off, k_tiled + off, vbs, 1, Nc, nh, D,
+                                              topk, idx, nullptr, 0.0f, 0.0f, ws,
+                                              static_cast<hipStream_t>(stream), NH);
+      if (e != hipSuccess) return launched(e, "select_noalloc");
+    }
+  return ok();
 }
 
 int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,

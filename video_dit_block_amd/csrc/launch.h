@@ -34,12 +34,14 @@ SelectWorkspace select_workspace(int B, int NH, int Nc, int D);
 // Selector pieces: mean of the real rows of every cube into fp32
 // [B][NH][Nc][D] (launch_pool: one tensor into xc; launch_pool_scores: q and k
 // into the workspace's Qc and Kc, then S = Qc . Kc^T), and the per-row top-k
-// (with the CDF count when valid != nullptr) over S [BH][Nc][Nc].
+// (with the CDF count when valid != nullptr) over S [BH][Nc][Nc]. row_nh > 0:
+// the tiled rows hold row_nh heads, of which the NH from the given pointers
+// on are pooled (0 = NH).
 hipError_t launch_pool(const uint16_t* x_tiled, const int32_t* vbs, int B, int Nc, int NH,
                        int D, float* xc, hipStream_t stream);
 hipError_t launch_pool_scores(const uint16_t* q_tiled, const uint16_t* k_tiled,
                               const int32_t* vbs, int B, int Nc, int NH, int D,
-                              void* workspace, hipStream_t stream);
+                              void* workspace, hipStream_t stream, int row_nh = 0);
 hipError_t launch_topk(const float* s, int BH, int Nc, int topk, int32_t* topk_idx,
                        int32_t* valid, float scale, float tau, hipStream_t stream);
 
@@ -57,11 +59,12 @@ hipError_t launch_gate_combine(const uint16_t* o_fine, const float* o_coarse,
                                const uint16_t* gate_c, const uint16_t* gate_f, uint16_t* out,
                                int B, int Nc, int NH, int D, hipStream_t stream);
 
-// valid != nullptr: also write the CDF count per row (scale, tau).
+// valid != nullptr: also write the CDF count per row (scale, tau). row_nh as
+// for launch_pool_scores.
 hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          const int32_t* vbs, int B, int Nc, int NH, int D,
                          int topk, int32_t* topk_idx, int32_t* valid, float scale, float tau,
-                         void* workspace, hipStream_t stream);
+                         void* workspace, hipStream_t stream, int row_nh = 0);
 
 // Workspace carve-up of vsa_fwd: an fp16 copy of v in the tiled layout, the
 // tile lists of the units ([B*NH*Nq][list_stride] pairs of uint32 quarters),

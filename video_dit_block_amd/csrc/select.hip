@@ -65,17 +65,20 @@ struct PoolArgs {
 // grid (Nc * splits, B, n_tensors), splits = ceil(cpr / kPoolThreads): each
 // lane owns one 16-byte column chunk (8 channels of one head) of the cube's
 // token rows and sums its real rows in fp32, kPoolUnroll rows in flight.
-// Output layout [B][NH][Nc][D] fp32.
+// The NH pooled heads are the first NH of each source row of row_cpr chunks
+// (row_cpr = NH * D / 8 unless the source holds more heads). Output layout
+// [B][NH][Nc][D] fp32.
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a, const int32_t* __restrict__ vbs,
-                                                           int Nc, int NH, int D, int splits) {
+                                                           int Nc, int NH, int D, int splits,
+                                                           int row_cpr) {
   const int c = blockIdx.x / splits, split = blockIdx.x - c * splits, b = blockIdx.y;
-  const int cpr = NH * D / 8;  // 16-byte chunks (8 bf16) per token row
+  const int cpr = NH * D / 8;  // 16-byte chunks (8 bf16) of the pooled heads
   const int col = split * kPoolThreads + threadIdx.x;
   if (col >= cpr) return;
   const u32x4* __restrict__ x = a.x[blockIdx.z];
   float* __restrict__ xc = a.xc[blockIdx.z];
   const int n = min(max(vbs[c], 0), kCube);  // clamped: never reads past the cube
-  const u32x4* __restrict__ base = x + ((size_t)b * Nc + c) * kCube * cpr + col;
+  const u32x4* __restrict__ base = x + ((size_t)b * Nc + c) * kCube * row_cpr + col;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   auto add = [&](const u32x4 t) __attribute__((always_inline)) {
 #pragma unroll
@@ -88,11 +91,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a, const in
   for (; u + kPoolUnroll <= n; u += kPoolUnroll) {
     u32x4 t[kPoolUnroll];
 #pragma unroll
-    for (int i = 0; i < kPoolUnroll; ++i) t[i] = __builtin_nontemporal_load(base + (size_t)(u + i) * cpr);
+    for (int i = 0; i < kPoolUnroll; ++i) t[i] = __builtin_nontemporal_load(base + (size_t)(u + i) * row_cpr);
 #pragma unroll
     for (int i = 0; i < kPoolUnroll; ++i) add(t[i]);
   }
-  for (; u < n; ++u) add(__builtin_nontemporal_load(base + (size_t)u * cpr));
+  for (; u < n; ++u) add(__builtin_nontemporal_load(base + (size_t)u * row_cpr));
   const int elem = col * 8;
   const int h = elem / D, d = elem - h * D;
   float* dst = xc + (((size_t)b * NH + h) * Nc + c) * D + d;
@@ -106,11 +109,11 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(PoolArgs a, const in
 }
 
 hipError_t pool_launch(const PoolArgs& a, int n_tensors, const int32_t* vbs, int B, int Nc,
-                       int NH, int D, hipStream_t stream) {
+                       int NH, int D, hipStream_t stream, int row_nh) {
   const int cpr = NH * D / 8;
   const int splits = (cpr + kPoolThreads - 1) / kPoolThreads;
   hipLaunchKernelGGL(pool_kernel, dim3(Nc * splits, B, n_tensors), dim3(kPoolThreads), 0, stream,
-                     a, vbs, Nc, NH, D, splits);
+                     a, vbs, Nc, NH, D, splits, row_nh * D / 8);
   return hipGetLastError();
 }
 
@@ -464,7 +467,7 @@ hipError_t launch_pool(const uint16_t* x_tiled, const int32_t* vbs, int B, int N
   PoolArgs a = {};
   a.x[0] = reinterpret_cast<const u32x4*>(x_tiled);
   a.xc[0] = xc;
-  return pool_launch(a, 1, vbs, B, Nc, NH, D, stream);
+  return pool_launch(a, 1, vbs, B, Nc, NH, D, stream, NH);
 }
 
 SelectWorkspace select_workspace(int B, int NH, int Nc, int D) {
@@ -479,7 +482,7 @@ SelectWorkspace select_workspace(int B, int NH, int Nc, int D) {
 
 hipError_t launch_pool_scores(const uint16_t* q_tiled, const uint16_t* k_tiled,
                               const int32_t* vbs, int B, int Nc, int NH, int D,
-                              void* workspace, hipStream_t stream) {
+                              void* workspace, hipStream_t stream, int row_nh) {
   const SelectWorkspace w = select_workspace(B, NH, Nc, D);
   char* ws = static_cast<char*>(workspace);
   float* qc = reinterpret_cast<float*>(ws + w.qc_off);
@@ -491,7 +494,7 @@ hipError_t launch_pool_scores(const uint16_t* q_tiled, const uint16_t* k_tiled,
   a.x[1] = reinterpret_cast<const u32x4*>(k_tiled);
   a.xc[0] = qc;
   a.xc[1] = kc;
-  hipError_t e = pool_launch(a, 2, vbs, B, Nc, NH, D, stream);
+  hipError_t e = pool_launch(a, 2, vbs, B, Nc, NH, D, stream, row_nh > 0 ? row_nh : NH);
   if (e != hipSuccess) return e;
 
   const int nt = (Nc + kScoreTile - 1) / kScoreTile;
@@ -536,8 +539,9 @@ hipError_t launch_topk(const float* s, int BH, int Nc, int topk, int32_t* topk_i
 hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          const int32_t* vbs, int B, int Nc, int NH, int D,
                          int topk, int32_t* topk_idx, int32_t* valid, float scale, float tau,
-                         void* workspace, hipStream_t stream) {
-  hipError_t e = launch_pool_scores(q_tiled, k_tiled, vbs, B, Nc, NH, D, workspace, stream);
+                         void* workspace, hipStream_t stream, int row_nh) {
+  hipError_t e = launch_pool_scores(q_tiled, k_tiled, vbs, B, Nc, NH, D, workspace, stream,
+                                    row_nh);
   if (e != hipSuccess) return e;
   const float* s = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
                                                   select_workspace(B, NH, Nc, D).s_off);

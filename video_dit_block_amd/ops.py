@@ -35,6 +35,11 @@ def _i32(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be a contiguous int32 CUDA tensor")
 
 
+def _shape(t: torch.Tensor, shape: tuple, name: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def num_cubes(T: int, H: int, W: int) -> int:
     n = _lib.load().vsa_num_cubes(T, H, W)
     if n < 0:
@@ -145,6 +150,35 @@ def select(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk: int,
                                       workspace.numel() * workspace.element_size(), _stream()),
                "vsa_select")
     return out
+
+
+def select_noalloc(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk: int,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """The coarse selector without a workspace (vsa_select_noalloc): the same
+    topk_idx int32 (B, NH, Nc, topk) as ``select``, computed in the library's
+    static per-GPU scratch. With ``out`` given, nothing is allocated."""
+    _bf16(q_t, "q_t")
+    _bf16(k_t, "k_t")
+    _i32(vbs, "vbs")
+    B, S, NH, D = q_t.shape
+    Nc = S // CUBE
+    if k_t.shape != q_t.shape or S % CUBE:
+        raise ValueError("q_t and k_t must both be (B, Nc*64, NH, D)")
+    if vbs.numel() != Nc:
+        raise ValueError(f"vbs must hold Nc = {Nc} entries")
+    if out is None:
+        out = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=q_t.device)
+    _i32(out, "out")
+    _shape(out, (B, NH, Nc, topk), "out")
+    _lib.check(_lib.load().vsa_select_noalloc(q_t.data_ptr(), k_t.data_ptr(), vbs.data_ptr(), B,
+                                              Nc, NH, D, topk, out.data_ptr(), _stream()),
+               "vsa_select_noalloc")
+    return out
+
+
+def select_noalloc_max_bytes() -> int:
+    """Size of the static per-GPU scratch of select_noalloc."""
+    return int(_lib.load().vsa_select_noalloc_max_bytes())
 
 
 def select_cdf(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, max_k: int, tau: float,
