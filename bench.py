@@ -10,14 +10,19 @@ events on the stream the library launches on (torch's current stream).
 The headline figure is the fine forward (vsa_fwd): kernel-only, warmed,
 effective TFLOP/s = 4 * D * 64 * sum over (b, h, query cube) of the real
 tokens of the selected cubes, divided by its mean launch time. The same
-kernel is also timed at topk = all (dense). Further legs on the same tensors:
-the lookup-table path (cumulative-mass selector + vsa_fwd_lut with its row
+kernel is also timed at topk = all (dense) and over the sparsity sweep
+topk in {624, 312, 187, 78, 31}. Further legs on the same tensors: the
+lookup-table path (cumulative-mass selector + vsa_fwd_lut with its row
 statistics), the two-stage path (coarse output, gated combine), the fine
-kernel in Hilbert cube order, and the block mask -> LUT compaction. The CPU
-oracle is timed on a bounded sample of the same workload as a reported
+kernel in Hilbert cube order, and the block mask -> LUT compaction; then the
+whole path on the 720p HunyuanVideo-like workload. Context measured in the
+same run: the engine clock during the timed vsa_fwd loop (amdsmi samples),
+and two bf16 ceilings of this part, a bounded MFMA-only loop on random
+operands and a large hipBLASLt GEMM. The CPU oracle is timed on a bounded
+sample of the same workload, in one process per core, as a reported
 baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-hy720] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -32,8 +37,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, AMD's published figure
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+CPU_PROCS_MAX = 16          # host cores a one-GPU share of the box provides
 
 
 def profiled_traffic() -> float | None:
@@ -62,6 +68,13 @@ def fwd_flops(topk_idx: np.ndarray, vbs: np.ndarray, D: int) -> float:
     return 4.0 * D * 64.0 * float(sel_tokens)
 
 
+def fwd_flops_real_q(topk_idx: np.ndarray, vbs: np.ndarray, D: int) -> float:
+    """The stricter count: only the real rows of each query cube,
+    4 * D * vbs[c] * (real selected KV tokens), summed over units (Nq = Nkv)."""
+    sel = vbs[topk_idx].astype(np.int64).sum(axis=-1)          # (B, NH, Nq)
+    return 4.0 * D * float((sel * vbs[None, None, :].astype(np.int64)).sum())
+
+
 def lut_flops(kv_block_idx: np.ndarray, counts: np.ndarray, vbs: np.ndarray, D: int) -> float:
     """fwd_flops over the first counts[b, h, c] ids of each row."""
     used = np.arange(kv_block_idx.shape[-1]) < counts[..., None]
@@ -76,56 +89,200 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--fwd-reps", type=int, default=50,
                     help="extra back-to-back vsa_fwd launches timed for the kernel figure")
-    ap.add_argument("--sweep", action="store_true", help="also time topk in {624,312,187,78,31}")
-    ap.add_argument("--hy720", action="store_true",
-                    help="also time the whole path on the 720p HunyuanVideo-like workload")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the topk sweep {624, 312, 187, 78, 31}")
+    ap.add_argument("--no-hy720", action="store_true",
+                    help="skip the whole path on the 720p HunyuanVideo-like workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cdf-tau", type=float, default=0.9,
                     help="threshold of the cumulative-mass selector leg")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="fine-stage oracle seconds per CPU worker process")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only vsa_fwd launches (for profiler runs)")
     return ap.parse_args()
 
 
-def cpu_baseline(case, seconds: float) -> dict:
-    """Time the CPU oracle (as it stands) on whole heads of the workload until
-    about `seconds` of work; report effective TFLOP/s in the metric's unit."""
+_CPU_CASE = None  # the workload, inherited by the forked CPU workers
+
+
+def _cpu_worker(job):
+    """One CPU worker (one BLAS thread): tile head h with the oracle, time the
+    oracle's selector on it, then the oracle's fine stage over the head's
+    query cubes in order until `seconds` of fine-stage time."""
     import threadpoolctl
 
     import oracle
 
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] or [1])
-    done_units, flops, spent = 0, 0.0, 0.0
-    heads_used = 0
-    for h in range(case.NH):
-        q_t, vbs = oracle.tile(case.q[:, :, h:h + 1], case.T, case.H, case.W)
-        k_t, _ = oracle.tile(case.k[:, :, h:h + 1], case.T, case.H, case.W)
-        v_t, _ = oracle.tile(case.v[:, :, h:h + 1], case.T, case.H, case.W)
-        q64, k64, v64 = (oracle.decode_bf16(a) for a in (q_t, k_t, v_t))
+    h, seconds = job
+    case = _CPU_CASE
+    with threadpoolctl.threadpool_limits(1):
+        t0 = time.perf_counter()
+        tiled = [oracle.tile(x[:, :, h:h + 1], case.T, case.H, case.W) for x in (case.q, case.k,
+                                                                               case.v)]
+        vbs = tiled[0][1]
+        q64, k64, v64 = (oracle.decode_bf16(t[0]) for t in tiled)
+        t1 = time.perf_counter()
         idx, _ = oracle.select(q64, k64, vbs, case.topk)
-        heads_used += 1
-        for c in range(vbs.size):
-            t0 = time.perf_counter()
-            oracle.fwd_unit(q64, k64, v64, idx, vbs, 0, 0, c)
-            spent += time.perf_counter() - t0
-            flops += fwd_flops(idx[0, 0, c:c + 1], vbs, case.D)
-            done_units += 1
-            if spent >= seconds:
-                break
-        if spent >= seconds:
-            break
+        t2 = time.perf_counter()
+        units, flops = 0, 0.0
+        while units < vbs.size and time.perf_counter() - t2 < seconds:
+            oracle.fwd_unit(q64, k64, v64, idx, vbs, 0, 0, units)
+            flops += fwd_flops(idx[0, 0, units:units + 1], vbs, case.D)
+            units += 1
+        t3 = time.perf_counter()
+    return {"head": h, "tile_s": t1 - t0, "select_s": t2 - t1, "fwd_s": t3 - t2,
+            "units": units, "flops": flops, "head_flops": fwd_flops(idx, vbs, case.D)}
+
+
+def cpu_baseline(case, seconds: float) -> dict:
+    """The CPU oracle (as it stands, never tuned) on a bounded sample of the
+    workload: one worker process per host core (at most CPU_PROCS_MAX), one
+    BLAS thread each, each on its own head: the oracle's selector on the whole
+    head, then the oracle's fine stage over that head's first query cubes for
+    `seconds`. Reported in the metric's unit (effective TFLOP/s of the fine
+    stage, all workers together), with the single-process rate, the
+    whole-workload times extrapolated from the sample, and the CPU model.
+    Runs before anything touches the GPU (the workers are forked)."""
+    import multiprocessing as mp
+
+    global _CPU_CASE
+    _CPU_CASE = case
+    procs = max(1, min(CPU_PROCS_MAX, len(os.sched_getaffinity(0)), case.NH))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(procs) as pool:
+        res = pool.map(_cpu_worker, [(h, seconds) for h in range(procs)])
+    wall = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                     if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    rate_each = [r["flops"] / r["fwd_s"] for r in res]      # FLOP/s per process
+    agg = float(sum(rate_each))
+    whole_flops = float(np.mean([r["head_flops"] for r in res])) * case.NH
+    sel_head = float(np.mean([r["select_s"] for r in res]))
     return {
-        "value": flops / spent / 1e12,
+        "value": agg / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": procs,
         "kind": "oracle",
-        "sample": (f"float64 NumPy oracle fwd on {done_units} of {case.NH * 624} "
-                   f"(head, query-cube) units of the Wan workload ({heads_used} head(s), "
-                   f"oracle-selected top-{case.topk}); {spent:.1f} s of fwd time, "
-                   f"host cores visible {len(os.sched_getaffinity(0))}"),
+        "sample": (f"float64 NumPy oracle: {procs} worker processes (1 BLAS thread each) on "
+                   f"heads 0..{procs - 1} of the Wan workload; per worker the oracle selector "
+                   f"(top-{case.topk}) on its whole head, then the fine stage on its first "
+                   f"{min(r['units'] for r in res)}-{max(r['units'] for r in res)} query cubes "
+                   f"({seconds:.0f} s each); {sum(r['units'] for r in res)} of "
+                   f"{case.NH * 624} units in all, {wall:.1f} s wall"),
+        "cpu_model": model,
+        "host_cores_visible": len(os.sched_getaffinity(0)),
+        "blas_threads_per_process": 1,
+        "single_process_tflops": round(float(np.median(rate_each)) / 1e12, 5),
+        "fwd_whole_workload_s_extrapolated": {
+            "single_process": round(whole_flops / float(np.median(rate_each)), 1),
+            f"{procs}_processes": round(whole_flops / agg, 1)},
+        "selector_s_per_head": round(sel_head, 3),
+        "selector_whole_workload_s_extrapolated": {
+            "single_process": round(sel_head * case.NH, 2),
+            f"{procs}_processes": round(sel_head * case.NH / procs, 2)},
     }
+
+
+class ClockMeter:
+    """The engine clock while a loop runs: libvsa_probe.so's meter, one
+    one-wave workgroup per XCD on a second stream (default priority) for a
+    fixed span of the 100 MHz real-time counter, counting shader cycles
+    (s_memtime) meanwhile. Started just before the loop, with a span that
+    ends within it. The meter's waves hold a few slots of 8 CUs, so each loop
+    is timed without it and then repeated once with it for the clock."""
+
+    def __init__(self, torch, dev):
+        import ctypes
+
+        self.torch = torch
+        self.lib = ctypes.CDLL(os.path.join(ROOT, "video_dit_block_amd", "libvsa_probe.so"))
+        self.lib.vsa_probe_clock.restype = ctypes.c_int32
+        self.lib.vsa_probe_clock.argtypes = [ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+        self.slots = 8
+        self.buf = torch.zeros(2 * self.slots, dtype=torch.int64, device=dev)
+        self.stream = torch.cuda.Stream(device=dev)
+
+    def start(self, span_ms: float):
+        self.span_ms = span_ms
+        self.stream.wait_stream(self.torch.cuda.current_stream())
+        st = self.lib.vsa_probe_clock(self.slots, int(span_ms * 1e5), self.buf.data_ptr(),
+                                      self.stream.cuda_stream)
+        assert st == 0, st
+
+    def stop(self) -> dict:
+        self.torch.cuda.synchronize()
+        v = self.buf.cpu().numpy().reshape(self.slots, 2).astype(np.float64)
+        mhz = v[:, 0] / v[:, 1] * 100.0
+        return {"source": "shader cycle counter (s_memtime) over the 100 MHz real-time counter, "
+                          f"one one-wave workgroup per XCD on a second stream, {self.span_ms:.0f} "
+                          "ms inside a repeat of the timed loop",
+                "mean_mhz": round(float(mhz.mean()), 1), "min_mhz": round(float(mhz.min()), 1),
+                "max_mhz": round(float(mhz.max()), 1)}
+
+
+def bf16_ceilings(torch, dev, clock) -> dict:
+    """Two measured bf16 rates of this part, context for the fine kernel's:
+    a bounded MFMA-only loop on random operands (libvsa_probe.so, about 0.5 s)
+    and torch.matmul bf16 at 16384^3 (hipBLASLt), each timed with events after
+    a warm-up long enough for the clock to settle."""
+    import ctypes
+
+    out = {}
+    lib = ctypes.CDLL(os.path.join(ROOT, "video_dit_block_amd", "libvsa_probe.so"))
+    lib.vsa_probe_mfma.restype = ctypes.c_int32
+    lib.vsa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.vsa_probe_mfma_flop.restype = ctypes.c_double
+    lib.vsa_probe_mfma_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    slots, blocks, iters = 64, 1024, 4000
+    gen = torch.Generator(device=dev).manual_seed(11)
+    src = torch.randn((slots, 16384), generator=gen, device=dev).to(torch.bfloat16)
+    res = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    run = lambda: lib.vsa_probe_mfma(src.data_ptr(), slots, blocks, iters, res.data_ptr(),
+                                     stream)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(8):                     # about 0.1 s: the clock settles
+        assert run() == 0
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(20):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 20
+    clock.start(span_ms=100.0)            # the same loop again, for its clock only
+    for _ in range(20):
+        run()
+    out["mfma_loop_clock"] = clock.stop()
+    out["mfma_loop_tflops"] = round(lib.vsa_probe_mfma_flop(blocks, iters) / ms / 1e9, 1)
+    out["mfma_loop"] = ("v_mfma_f32_32x32x16_bf16 on random bf16 operands read from LDS, "
+                        "4 waves per workgroup, 4 workgroups per CU, 1024 workgroups")
+    n = 16384
+    a = torch.randn((n, n), generator=gen, device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=gen, device=dev).to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0.record()
+    for _ in range(8):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 8
+    clock.start(span_ms=30.0)             # the same loop again, for its clock only
+    for _ in range(8):
+        torch.matmul(a, b, out=c)
+    out["gemm_clock"] = clock.stop()
+    out["gemm_bf16_16384_tflops"] = round(2.0 * n ** 3 / ms / 1e9, 1)
+    del a, b, c, src, res
+    return out
 
 
 def time_pipeline(case, vsa, torch, reps: int) -> dict:
@@ -197,12 +354,17 @@ def main():
     import synth
     import video_dit_block_amd as vsa
 
+    print("[bench] generating the Wan-shaped input (seed 2)", file=sys.stderr, flush=True)
+    case = synth.wan()
+    cpu = None
+    if not args.no_cpu and not args.fwd_only:
+        # before any GPU call: the CPU workers are forked from this process
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, args.cpu_seconds)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    print("[bench] generating the Wan-shaped input (seed 2)", file=sys.stderr, flush=True)
-    case = synth.wan()
     T, H, W, NH, D, B, topk = case.T, case.H, case.W, case.NH, case.D, case.B, case.topk
     to_gpu = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     q, k, v = to_gpu(case.q), to_gpu(case.k), to_gpu(case.v)
@@ -268,7 +430,8 @@ def main():
     parts /= args.steps
     step_ms = float(parts.sum())
 
-    # the fine forward alone, back to back (kernel-only, warmed)
+    # the fine forward alone, back to back (kernel-only, warmed), with the
+    # engine clock sampled while it runs
     e0, e1 = ev(), ev()
     e0.record()
     for _ in range(args.fwd_reps):
@@ -276,6 +439,12 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     fwd_ms = e0.elapsed_time(e1) / args.fwd_reps
+    # the same loop again with the clock meter beside it (its figure only)
+    clock = ClockMeter(torch, dev)
+    clock.start(span_ms=0.7 * args.fwd_reps * fwd_ms)
+    for _ in range(args.fwd_reps):
+        vsa.fwd(qt, kt, vt, idx, vbs, out=out, workspace=wsf)
+    clock_fwd = clock.stop()
     # the same calls one at a time, each between its own pair of events
     pairs = [(ev(), ev()) for _ in range(args.fwd_reps)]
     for a, b in pairs:
@@ -288,6 +457,7 @@ def main():
     vbs_h = vbs.cpu().numpy()
     idx_h = idx.cpu().numpy()
     flops = fwd_flops(idx_h, vbs_h, D)
+    flops_real_q = fwd_flops_real_q(idx_h, vbs_h, D)
     tflops = flops / (fwd_ms * 1e-3) / 1e12
     finite = bool(torch.isfinite(out.float()).all())
 
@@ -307,7 +477,7 @@ def main():
     dense_flops = fwd_flops(idx_all.cpu().numpy(), vbs_h, D)
 
     sweep = None
-    if args.sweep:
+    if not args.no_sweep:
         sweep = {}
         for kk in synth.SWEEP_TOPK:
             ik = idx_all[..., :kk].contiguous()
@@ -444,7 +614,8 @@ def main():
 
     # tiling traffic: read real rows, write all rows, per tensor
     tile_bytes = 3 * (T * H * W + S) * NH * D * 2
-    cpu = None if args.no_cpu else cpu_baseline(case, args.cpu_seconds)
+    print("[bench] bf16 ceilings", file=sys.stderr, flush=True)
+    ceilings = bf16_ceilings(torch, dev, clock)
 
     line = {
         "metric": "fine VSA fwd kernel ms + effective TFLOP/s (% bf16 peak), Wan2.2 shape, "
@@ -474,6 +645,14 @@ def main():
                             "calls": int(per_call.size)},
         "fwd_tflop": round(flops / 1e12, 4),
         "fwd_pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "peak_bf16_tflops": PEAK_BF16_TFLOPS,
+        "fwd_tflop_real_q": round(flops_real_q / 1e12, 4),
+        "fwd_pct_peak_real_q": round(100 * flops_real_q / (fwd_ms * 1e-3) / 1e12
+                                     / PEAK_BF16_TFLOPS, 2),
+        "clock_during_fwd": clock_fwd,
+        "bf16_ceilings": dict(ceilings, fwd_pct_of_mfma_loop=round(
+            100 * tflops / ceilings["mfma_loop_tflops"], 1), fwd_pct_of_gemm_bf16=round(
+            100 * tflops / ceilings["gemm_bf16_16384_tflops"], 1)),
         "fwd_finite": finite,
         "dense": {"topk": Nc, "ms": round(dense_ms, 4), "tflop": round(dense_flops / 1e12, 3),
                   "tflops": round(dense_flops / dense_ms / 1e9, 1),
@@ -492,7 +671,7 @@ def main():
     line["order_mask"] = order_mask
     if sweep is not None:
         line["sweep"] = sweep
-    if args.hy720:
+    if not args.no_hy720:
         del qt, kt, vt, out, out_nat, wsf, ws, idx
         torch.cuda.empty_cache()
         print("[bench] 720p workload", file=sys.stderr, flush=True)

@@ -18,8 +18,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
+# measurement aid of the benchmark (a bf16 MFMA ceiling loop), not the VSA path
+PROBE_LIB = os.path.join(PKG, "libvsa_probe.so")
 
 SOURCES = ["api.hip", "tile.hip", "select.hip", "fwd.hip", "coarse.hip", "lut.hip", "validate.hip"]
+PROBE_SOURCES = ["mfma_peak.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -49,26 +52,29 @@ def _run(cmd: list[str]) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libvsa.so; returns the library path."""
+    """Compile every source, link libvsa.so and the benchmark's probe library;
+    returns the path of libvsa.so."""
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    objs = {}
     cmds = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
+        objs[src] = obj
         cmds.append([cc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
         for cmd, fut in zip(cmds, [ex.submit(_run, c) for c in cmds]):
             if verbose:
                 print(" ".join(cmd))
             fut.result()
-    tmp = LIB + ".tmp"
-    link = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(link))
-    _run(link)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        link = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[objs[s] for s in srcs],
+                "-o", tmp]
+        if verbose:
+            print(" ".join(link))
+        _run(link)
+        os.replace(tmp, lib)
     return LIB
 
 
