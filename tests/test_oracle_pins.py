@@ -59,11 +59,10 @@ def test_vbs_tiny_row_major_order():
     assert oracle.cube_sizes(5, 6, 7).tolist() == expect
 
 
-@pytest.mark.parametrize("grid", [(5, 6, 7), (4, 4, 4), (1, 1, 1), (9, 3, 5), (8, 13, 2)])
-def test_tile_permutation_independent_derivation(grid):
+def tile_order_pin(slot_tokens_fn, grid) -> bool:
     """Token -> slot by sorting tokens on (cube id, t, h, w): an independent
     formulation of the cube-major order with real tokens first, row-major inside
-    the clipped cube."""
+    the clipped cube. True when slot_tokens_fn agrees with it."""
     T, H, W = grid
     Nt, Nh, Nw = -(-T // 4), -(-H // 4), -(-W // 4)
     t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
@@ -75,7 +74,12 @@ def test_tile_permutation_independent_derivation(grid):
     for c in range(Nt * Nh * Nw):
         members = nat[order][cube[order] == c]
         expect[c, :members.size] = members
-    np.testing.assert_array_equal(oracle.slot_tokens(T, H, W), expect)
+    return np.array_equal(slot_tokens_fn(T, H, W), expect)
+
+
+@pytest.mark.parametrize("grid", [(5, 6, 7), (4, 4, 4), (1, 1, 1), (9, 3, 5), (8, 13, 2)])
+def test_tile_permutation_independent_derivation(grid):
+    assert tile_order_pin(oracle.slot_tokens, grid)
 
 
 def test_tile_untile_roundtrip_bitwise_and_zero_pads():
@@ -325,13 +329,22 @@ def _rank_count_topk(row, k):
     return out
 
 
-def test_topk_matches_rank_counting_with_ties():
-    S = RNG.integers(-3, 4, size=(1, 2, 12, 17)).astype(np.float64)   # many ties
+def topk_tie_pin(topk_fn) -> bool:
+    """Rows full of ties (integer scores in [-3, 3]): topk_fn must give, for
+    k = 1, 5, 17, exactly the brute-force rank count (score descending, equal
+    scores by ascending id)."""
+    S = np.random.default_rng(77).integers(-3, 4, size=(1, 2, 12, 17)).astype(np.float64)
     for k in (1, 5, 17):
-        idx = oracle.topk_select(S, k)
+        idx = topk_fn(S, k)
         for h in range(2):
             for i in range(12):
-                np.testing.assert_array_equal(idx[0, h, i], _rank_count_topk(S[0, h, i], k))
+                if not np.array_equal(idx[0, h, i], _rank_count_topk(S[0, h, i], k)):
+                    return False
+    return True
+
+
+def test_topk_matches_rank_counting_with_ties():
+    assert topk_tie_pin(oracle.topk_select)
 
 
 def test_topk_all_is_permutation_and_descending():
@@ -585,47 +598,62 @@ def test_coarse_output_no_real_key_cube_is_zero():
     assert np.array_equal(oracle.coarse_output(x, x, x, vbs), np.zeros((1, 2, 3, 4)))
 
 
-def test_gated_combine_brute_force_and_special_gates():
+def combine_pin(combine_fn) -> bool:
     """VSA blog, "Two-Stage Architecture": out = g_c * Oc + g_f * O_fine with
     the coarse row broadcast to its cube's 64 rows; checked element by element,
     and gates (1, 0) / (0, 1) give the branches themselves."""
+    rng = np.random.default_rng(21)
     B, Nc, NH, D = 2, 3, 2, 4
     S = Nc * 64
-    of, gc, gf = (_randn(B, S, NH, D) for _ in range(3))
-    oc = _randn(B, NH, Nc, D)
-    got = oracle.gated_combine(of, oc, gc, gf)
+    of, gc, gf = (rng.standard_normal((B, S, NH, D)) for _ in range(3))
+    oc = rng.standard_normal((B, NH, Nc, D))
+    got = combine_fn(of, oc, gc, gf)
     for b in range(B):
         for s in range(0, S, 7):
             for h in range(NH):
                 for d in range(D):
                     want = gc[b, s, h, d] * oc[b, h, s // 64, d] + gf[b, s, h, d] * of[b, s, h, d]
-                    assert got[b, s, h, d] == want
+                    if got[b, s, h, d] != want:
+                        return False
     one, zero = np.ones_like(of), np.zeros_like(of)
-    assert np.array_equal(oracle.gated_combine(of, oc, zero, one), of)
-    bc = oracle.gated_combine(of, oc, one, zero)
-    for s in range(S):
-        assert np.array_equal(bc[:, s], oc[:, :, s // 64])
+    if not np.array_equal(combine_fn(of, oc, zero, one), of):
+        return False
+    bc = combine_fn(of, oc, one, zero)
+    return all(np.array_equal(bc[:, s], oc[:, :, s // 64]) for s in range(S))
+
+
+def test_gated_combine_brute_force_and_special_gates():
+    assert combine_pin(oracle.gated_combine)
 
 
 # --------------------------------------------- cube order (SFC), mask -> LUT
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
-def test_hilbert_box_order_is_a_unit_step_hierarchical_path(bits):
+def hilbert_pin(index_fn, bits) -> bool:
     """Defining properties of the 3D Hilbert curve on a 2^b box: the indices are
     a permutation of [0, 8^b); the path starts at the origin; consecutive cells
     are face neighbours; every aligned 2^k sub-box is visited contiguously."""
     n = 1 << bits
     cells = [(x, y, z) for x in range(n) for y in range(n) for z in range(n)]
-    idx = [oracle.hilbert_index_3d(*c, bits) for c in cells]
-    assert sorted(idx) == list(range(n ** 3))
+    idx = [index_fn(*c, bits) for c in cells]
+    if sorted(idx) != list(range(n ** 3)):
+        return False
     path = [cells[i] for i in np.argsort(idx)]
-    assert path[0] == (0, 0, 0)
+    if path[0] != (0, 0, 0):
+        return False
     steps = np.abs(np.diff(np.asarray(path), axis=0)).sum(axis=1)
-    assert np.all(steps == 1)
+    if not np.all(steps == 1):
+        return False
     for k in range(1, bits):
         blocks = [tuple(v >> k for v in c) for c in path]
         runs = [b for i, b in enumerate(blocks) if i == 0 or b != blocks[i - 1]]
-        assert len(runs) == len(set(runs)) == (n >> k) ** 3
+        if not len(runs) == len(set(runs)) == (n >> k) ** 3:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_hilbert_box_order_is_a_unit_step_hierarchical_path(bits):
+    assert hilbert_pin(oracle.hilbert_index_3d, bits)
 
 
 def test_cube_order_restricts_the_box_curve():

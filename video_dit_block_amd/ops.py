@@ -36,8 +36,15 @@ def _i32(t: torch.Tensor, name: str) -> None:
 
 
 def _shape(t: torch.Tensor, shape: tuple, name: str) -> None:
+    """Caller-supplied buffers must have exactly the shape the C call writes
+    (a smaller one would be written past its end on the device)."""
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _numel(t: torch.Tensor, n: int, name: str) -> None:
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} entries, got {t.numel()}")
 
 
 def num_cubes(T: int, H: int, W: int) -> int:
@@ -89,9 +96,11 @@ def tile(x: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = Non
     if out is None:
         out = torch.empty((B, nc * CUBE, NH, D), dtype=torch.bfloat16, device=x.device)
     _bf16(out, "out")
+    _shape(out, (B, nc * CUBE, NH, D), "out")
     if vbs is None:
         vbs = torch.empty(nc, dtype=torch.int32, device=x.device)
     _i32(vbs, "vbs")
+    _numel(vbs, nc, "vbs")
     _order(order, nc)
     if order is None:
         _lib.check(_lib.load().vsa_tile(x.data_ptr(), out.data_ptr(), vbs.data_ptr(), B, T, H, W,
@@ -114,6 +123,7 @@ def untile(y: torch.Tensor, T: int, H: int, W: int, out: torch.Tensor | None = N
     if out is None:
         out = torch.empty((B, T * H * W, NH, D), dtype=torch.bfloat16, device=y.device)
     _bf16(out, "out")
+    _shape(out, (B, T * H * W, NH, D), "out")
     _order(order, S // CUBE)
     if order is None:
         _lib.check(_lib.load().vsa_untile(y.data_ptr(), out.data_ptr(), B, T, H, W, NH, D,
@@ -139,12 +149,14 @@ def select(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk: int,
     Nc = S // CUBE
     if k_t.shape != q_t.shape or S % CUBE:
         raise ValueError("q_t and k_t must both be (B, Nc*64, NH, D)")
+    _numel(vbs, Nc, "vbs")
     need = select_workspace_bytes(B, NH, Nc, D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_t.device)
     if out is None:
         out = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=q_t.device)
     _i32(out, "out")
+    _shape(out, (B, NH, Nc, topk), "out")
     _lib.check(_lib.load().vsa_select(q_t.data_ptr(), k_t.data_ptr(), vbs.data_ptr(), B, Nc, NH,
                                       D, topk, out.data_ptr(), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), _stream()),
@@ -164,8 +176,7 @@ def select_noalloc(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, topk
     Nc = S // CUBE
     if k_t.shape != q_t.shape or S % CUBE:
         raise ValueError("q_t and k_t must both be (B, Nc*64, NH, D)")
-    if vbs.numel() != Nc:
-        raise ValueError(f"vbs must hold Nc = {Nc} entries")
+    _numel(vbs, Nc, "vbs")
     if out is None:
         out = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=q_t.device)
     _i32(out, "out")
@@ -192,6 +203,7 @@ def select_cdf(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, max_k: i
     Nc = S // CUBE
     if k_t.shape != q_t.shape or S % CUBE:
         raise ValueError("q_t and k_t must both be (B, Nc*64, NH, D)")
+    _numel(vbs, Nc, "vbs")
     if workspace is None:
         workspace = torch.empty(select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8,
                                 device=q_t.device)
@@ -234,6 +246,7 @@ def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch
     if out is None:
         out = torch.empty_like(q_t)
     _bf16(out, "out")
+    _shape(out, tuple(q_t.shape), "out")
     scale = 0.0 if sm_scale is None else float(sm_scale)
     if workspace is None:
         workspace = torch.empty(fwd_workspace_bytes(B, Nq, Nkv, NH, D, topk),
@@ -310,6 +323,7 @@ def coarse(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, vbs: torch.T
     Nc = S // CUBE
     if k_t.shape != q_t.shape or v_t.shape != q_t.shape or S % CUBE:
         raise ValueError("q_t, k_t and v_t must all be (B, Nc*64, NH, D)")
+    _numel(vbs, Nc, "vbs")
     if workspace is None:
         workspace = torch.empty(coarse_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8,
                                 device=q_t.device)
