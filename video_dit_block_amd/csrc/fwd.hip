@@ -182,7 +182,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // l%32+32 (v_permlane32_swap exchanges the halves of two registers).
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  // the middle of (a, b, +inf) is max(a, b): one instruction, where fmaxf would
+  // first quieten both operands (the values are never NaN here)
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]),
+                                 __builtin_huge_valf());
 }
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -467,7 +470,9 @@ __global__ __launch_bounds__(kOrderThreads) void order_rank_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <int D>
+// kStats: the row statistics (lse, max_prob) are written; the plain forward
+// skips the bookkeeping of the exact row maximum that only max_prob needs.
+template <int D, bool kStats>
 __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v16, const uint32_t* __restrict__ list,
@@ -602,6 +607,8 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   // against; l_run: running sum of exp2((s - m_ref) * scale_log2); alpha and
   // need_rescale: the pending O rescale after a raise of m_ref
   float m_ref = kNegInf, l_run = 0.0f, alpha = 1.0f;
+  // a tile max above m_lim = m_ref + kRescaleThreshold / c raises m_ref
+  float m_lim = kNegInf;
   float m_row = kNegInf;  // the row's largest score so far (for max_prob)
   bool need_rescale = false;
   const floatx16 zero16 = {};
@@ -650,13 +657,15 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = halves_max(mx);
-    m_row = fmaxf(m_row, mx);
-    const bool up = mx * scale_log2 > m_ref * scale_log2 + kRescaleThreshold;
+    if (kStats) m_row = fmaxf(m_row, mx);
+    const bool up = mx > m_lim;
     need_rescale = __builtin_amdgcn_ballot_w64(up) != 0;
-    if (need_rescale) {
+    if (need_rescale) {  // rare: a real branch (the asm keeps it from being flattened)
+      asm volatile("");
       const float m_new = up ? mx : m_ref;
       alpha = m_ref == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
       m_ref = m_new;
+      m_lim = m_ref + kRescaleThreshold / scale_log2;
       l_run *= alpha;
     }
   };
@@ -780,7 +789,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   // 1 / sum exp2((s - m_row) c) = exp2((m_row - m_ref) c + kPShift) / l_run.
   if (g == 0 && lse != nullptr)
     lse[srow] = (m_ref * scale_log2 - kPShift + __log2f(l_run)) * 0.69314718055994531f;
-  if (g == 0 && max_prob != nullptr)
+  if (kStats && g == 0 && max_prob != nullptr)
     max_prob[srow] = __builtin_amdgcn_exp2f((m_row - m_ref) * scale_log2 + kPShift) / l_run;
 
   // ---- epilogue: lane holds O^T[d][row] for d = 32 db + 8 (r/4) + 4 g + r%4;
@@ -866,14 +875,19 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  if (D == 128)
-    hipLaunchKernelGGL(fwd_kernel<128>, dim3(n_units), dim3(FwdShape<128>::kThreads), 0, stream,
-                       q, k, v16, list, counts, order, vexp, out, lse, max_prob, Nq, Nkv, NH,
-                       w.list_stride, scale_log2, n_units);
-  else
-    hipLaunchKernelGGL(fwd_kernel<64>, dim3(n_units), dim3(FwdShape<64>::kThreads), 0, stream,
-                       q, k, v16, list, counts, order, vexp, out, lse, max_prob, Nq, Nkv, NH,
-                       w.list_stride, scale_log2, n_units);
+  const bool stats = lse != nullptr || max_prob != nullptr;
+#define VSA_FWD_LAUNCH(DD, ST)                                                                 \
+  hipLaunchKernelGGL((fwd_kernel<DD, ST>), dim3(n_units), dim3(FwdShape<DD>::kThreads), 0, stream, \
+                     q, k, v16, list, counts, order, vexp, out, lse, max_prob, Nq, Nkv, NH,     \
+                     w.list_stride, scale_log2, n_units)
+  if (D == 128) {
+    if (stats) VSA_FWD_LAUNCH(128, true);
+    else VSA_FWD_LAUNCH(128, false);
+  } else {
+    if (stats) VSA_FWD_LAUNCH(64, true);
+    else VSA_FWD_LAUNCH(64, false);
+  }
+#undef VSA_FWD_LAUNCH
   return hipGetLastError();
 }
 
