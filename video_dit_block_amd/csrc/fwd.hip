@@ -182,10 +182,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // l%32+32 (v_permlane32_swap exchanges the halves of two registers).
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  // the middle of (a, b, +inf) is max(a, b): one instruction, where fmaxf would
-  // first quieten both operands (the values are never NaN here)
-  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]),
-                                 __builtin_huge_valf());
+  // one v_max_f32: fmaxf would first quieten both operands (a v_max of each
+  // with itself); the values here are never NaN
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return m;
 }
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
