@@ -16,17 +16,21 @@ lookup-table path (cumulative-mass selector + vsa_fwd_lut with its row
 statistics), the two-stage path (coarse output, gated combine), the fine
 kernel in Hilbert cube order, and the block mask -> LUT compaction; then the
 whole path on the 720p HunyuanVideo-like workload. Context measured in the
-same run: the engine clock during the timed vsa_fwd loop (amdsmi samples),
-and two bf16 ceilings of this part, a bounded MFMA-only loop on random
-operands and a large hipBLASLt GEMM. The CPU oracle is timed on a bounded
+same run: the engine clock during the timed vsa_fwd loop (a shader-cycle
+meter on a second stream, in a repeat of the loop), and two bf16 ceilings of
+this part, a bounded MFMA-only loop on random operands and a large hipBLASLt
+GEMM. The CPU oracle is timed on a bounded
 sample of the same workload, in one process per core, as a reported
 baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-hy720] [--no-cpu]
+       python bench.py --fwd-only [--fwd-workload wan|hy720] ...   (profiler mode: vsa_fwd
+           launches, a 1 GiB copy that calibrates the HBM counters, LDS conflict controls)
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -42,22 +46,33 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 CPU_PROCS_MAX = 16          # host cores a one-GPU share of the box provides
 
 
+def code_digest(path: str) -> str:
+    """SHA-256 of a C++/HIP source with its comments removed and every run of
+    whitespace folded to one space: it changes with the code, not with the
+    comments."""
+    import hashlib
+    import re
+
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def profiled_traffic() -> float | None:
     """HBM bytes per vsa_fwd launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, calibrated against a 1 GiB copy), or None when the
-    fine kernel's source has changed since those counters were taken."""
-    import hashlib
-
+    fine kernel's code has changed since those counters were taken."""
     prof = os.path.join(ROOT, "profiles", "fwd_kernel_wan.md")
     src = os.path.join(ROOT, "video_dit_block_amd", "csrc", "fwd.hip")
     try:
         fields = dict(line.split(": ", 1) for line in open(prof).read().splitlines()
-                      if line.split(": ", 1)[0] in ("fwd_source_sha256", "fetch_bytes_per_launch",
+                      if line.split(": ", 1)[0] in ("fwd_code_sha256", "fetch_bytes_per_launch",
                                                     "write_bytes_per_launch"))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = code_digest(src)
     except (OSError, ValueError):
         return None
-    if fields.get("fwd_source_sha256") != sha:
+    if fields.get("fwd_code_sha256") != digest:
         return None
     return float(fields["fetch_bytes_per_launch"]) + float(fields["write_bytes_per_launch"])
 
@@ -100,6 +115,8 @@ def parse():
                     help="fine-stage oracle seconds per CPU worker process")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time only vsa_fwd launches (for profiler runs)")
+    ap.add_argument("--fwd-workload", choices=("wan", "hy720"), default="wan",
+                    help="workload of the --fwd-only launches")
     return ap.parse_args()
 
 
@@ -354,8 +371,12 @@ def main():
     import synth
     import video_dit_block_amd as vsa
 
-    print("[bench] generating the Wan-shaped input (seed 2)", file=sys.stderr, flush=True)
-    case = synth.wan()
+    if args.fwd_only and args.fwd_workload == "hy720":
+        print("[bench] generating the 720p input", file=sys.stderr, flush=True)
+        case = synth.hy720()
+    else:
+        print("[bench] generating the Wan-shaped input (seed 2)", file=sys.stderr, flush=True)
+        case = synth.wan()
     cpu = None
     if not args.no_cpu and not args.fwd_only:
         # before any GPU call: the CPU workers are forked from this process
@@ -412,8 +433,23 @@ def main():
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"fwd_only": True, "launches": args.warmup + args.steps,
-                          "calibration_copy_bytes": 1 << 30}))
+        # controls for the LDS bank-conflict counter: the same reads laid out
+        # conflict-free (stride 1) and on few banks (stride 8), 4- and 16-byte
+        lib = ctypes.CDLL(os.path.join(ROOT, "video_dit_block_amd", "libvsa_probe.so"))
+        lib.vsa_probe_lds.restype = ctypes.c_int32
+        lib.vsa_probe_lds.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+        res = torch.empty(1024 * 64, dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+        for width in (4, 16):
+            for stride in (1, 8):
+                st = lib.vsa_probe_lds(width, stride, 1024, 1024, res.data_ptr(), stream)
+                if st != 0:
+                    raise RuntimeError(f"vsa_probe_lds failed: {st}")
+        torch.cuda.synchronize()
+        print(json.dumps({"fwd_only": True, "workload": case.name,
+                          "launches": args.warmup + args.steps,
+                          "calibration_copy_bytes": 1 << 30,
+                          "lds_controls": "width 4/16 x stride 1/8, 1024 x 1024 reads"}))
         return
 
     print("[bench] warmup", file=sys.stderr, flush=True)

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define VSA_ABI_VERSION 5
+#define VSA_ABI_VERSION 6
 #define VSA_CUBE 64
 
 typedef uint16_t vsa_bf16_t; /* raw bf16 bits */
@@ -216,16 +216,35 @@ int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
                        int32_t* valid_block_num, void* workspace, size_t workspace_bytes,
                        vsa_stream_t stream);
 
+/* Number of key-range splits S the fine stage uses for these sizes
+ * (split-KV): each (b, h, query cube) is computed as S items, item s over the
+ * selected cubes j with j * S / Nkv == s, run split-major inside each head so
+ * that the items resident at once share one key range of the head; a merge
+ * pass combines their partial softmax states (the result is that of the
+ * unsplit stage up to fp32 rounding order). kv_splits: 0 chooses (S > 1 only
+ * once one head's K plus its fp16 V copy, Nkv * 64 * D * 4 bytes, exceeds
+ * 32 MiB: about 16 MiB of them per split, at least 8 selected cubes per split
+ * on average, at most 16), 1 turns splitting off, 2..16 asks for that many.
+ * Rows of more than 1024 ids are never split. Returns 0 for invalid
+ * arguments (kv_splits outside [0, 16], topk outside [1, Nkv]). Host-only. */
+int32_t vsa_fwd_splits(int32_t Nkv, int32_t D, int32_t topk, int32_t kv_splits);
+
 /* Bytes of device workspace vsa_fwd needs for these sizes: an fp16 copy of v
  * in the tiled layout (B * Nkv * 64 * NH * D * 2 bytes), then, per (b, h,
  * query cube) (B * NH * Nq of them), the list of the 32-row tiles that hold
- * real tokens of its selected cubes ((2 * topk + 4) entries of two uint32),
- * its length (one int32), its dispatch rank (one int32) and the rank's sort
- * key (two int32); then the largest |v| of every (v pre-pass workgroup, head)
- * (B * Nkv * 8 * NH float32) and the per-(b, h) exponent of the fp16 copy
- * (B * NH int32), each part 256-byte aligned. Returns 0 for invalid sizes. */
+ * real tokens of its selected cubes ((2 * topk + 4 + (S > 1 ? S : 0))
+ * entries of two uint32), the first tile of each split and the tile count
+ * (S + 1 int32), its dispatch rank (one int32) and the rank's sort key (two
+ * int32); then the largest |v| of every (v pre-pass workgroup, head)
+ * (B * Nkv * 8 * NH float32), the per-(b, h) exponent of the fp16 copy
+ * (B * NH int32) and, with S > 1 splits (vsa_fwd_splits), the partial
+ * results (B * NH * Nq * S * 64 * (D + 4) float32), each part 256-byte
+ * aligned. Returns 0 for invalid sizes. The _ex form takes kv_splits as
+ * vsa_fwd_splits does; the plain form is kv_splits = 0. */
 size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
                                int32_t D, int32_t topk);
+size_t vsa_fwd_workspace_bytes_ex(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
+                                  int32_t D, int32_t topk, int32_t kv_splits);
 
 /* Fine stage: non-causal block-sparse attention (Wan2.2 Production Values
  * dataset card, section "Operator contract"; VSA blog, "Two-Stage
@@ -242,7 +261,8 @@ size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH,
  * e in [-90, 113]) and its output multiplied back by 2^e; values below 2^-14
  * (times 2^e) become fp16 subnormals, an absolute error under 2^-24 (times
  * 2^e), at most 2^-20 of the head's largest |v|. The output is rounded to
- * bf16 (nearest even). A row with no real key outputs 0.
+ * bf16 (nearest even). A row with no real key outputs 0. Large heads run
+ * in key-range splits (vsa_fwd_splits with kv_splits = 0).
  *   q         [B][Nq*64][NH][D] bf16, tiled order (padding rows are computed
  *             like real rows)
  *   k, v      [B][Nkv*64][NH][D] bf16, tiled order (padding values ignored)
@@ -302,6 +322,19 @@ int32_t vsa_fwd_lut(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* 
                     int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
                     int32_t max_kv, float sm_scale, void* workspace,
                     size_t workspace_bytes, vsa_stream_t stream);
+
+/* vsa_fwd_lut with the number of key-range splits chosen by the caller
+ * (kv_splits as for vsa_fwd_splits: 0 = chosen from the sizes, as
+ * vsa_fwd_lut does; 1 = none; 2..16). The workspace is
+ * vsa_fwd_workspace_bytes_ex(B, Nq, Nkv, NH, D, max_kv, kv_splits) bytes.
+ * Errors: as for vsa_fwd_lut, and VSA_ERR_RANGE for kv_splits outside
+ * [0, 16]. */
+int32_t vsa_fwd_lut_ex(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                       const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                       const int32_t* vbs, vsa_bf16_t* out, float* lse, float* max_prob,
+                       int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                       int32_t max_kv, float sm_scale, int32_t kv_splits, void* workspace,
+                       size_t workspace_bytes, vsa_stream_t stream);
 
 /* Bytes of device workspace vsa_coarse needs: the vsa_select workspace
  * (pooled q and k, the scores) followed by the pooled v (B * NH * Nc * D

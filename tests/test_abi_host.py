@@ -28,7 +28,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = _lib.load()
-    assert lib.vsa_abi_version() == 5
+    assert lib.vsa_abi_version() == 6
     for s, name in [(0, "VSA_OK"), (1, "VSA_ERR_NULL"), (2, "VSA_ERR_SHAPE"),
                     (3, "VSA_ERR_UNSUPPORTED"), (4, "VSA_ERR_RANGE"), (5, "VSA_ERR_WORKSPACE"),
                     (6, "VSA_ERR_HIP")]:
@@ -104,8 +104,8 @@ def test_fwd_validation():
     assert call(out=P + 2) == _lib.VSA_ERR_UNSUPPORTED
     # fp16 v (8 cubes x 64 rows x 2 heads x 64 x 2 bytes), then the tile
     # lists of the 16 (head, query cube) units ((2 * 3 + 4) tiles x 8 bytes
-    # each = 1280 bytes), then their lengths (16 int32 -> 256 after 256-byte
-    # rounding), their dispatch ranks (16 int32 -> 256) and the ranks' sort
+    # each = 1280 bytes), then their first and end tiles (16 x 2 int32 -> 256
+    # after 256-byte rounding), their dispatch ranks (16 int32 -> 256) and the ranks' sort
     # keys (16 x 2 int32 -> 256), then the largest |v| of every (v pre-pass
     # workgroup, head) (8 cubes x 8 workgroups x 2 heads float32 = 512) and
     # the per-head exponent of the fp16 copy (2 int32 -> 256)
@@ -117,6 +117,45 @@ def test_fwd_validation():
     # one batch of k must span < 4 GiB: Nkv * 64 * NH * D * 2 = Nkv * 16384 here
     assert call(Nkv=1 << 18, topk=3) == _lib.VSA_ERR_UNSUPPORTED
     assert call(ws=P + 128) == _lib.VSA_ERR_WORKSPACE
+
+
+def test_fwd_splits_choice_and_workspace():
+    """The key-range split count: none at the Wan shape (a head's K and fp16 V
+    copy, 624 x 64 x 128 x 4 bytes = 20 MB, stay under 32 MiB), 4 at the 720p
+    shape (1920 cubes: 63 MB in splits of about 16 MiB), at most topk / 8,
+    never for rows longer than 1024 ids; forced counts are taken as given.
+    With splits the workspace adds the partial results."""
+    lib = _lib.load()
+    assert lib.vsa_fwd_splits(624, 128, 78, 0) == 1
+    assert lib.vsa_fwd_splits(1920, 128, 192, 0) == 4
+    assert lib.vsa_fwd_splits(1920, 128, 24, 0) == 3
+    assert lib.vsa_fwd_splits(1920, 128, 8, 0) == 1
+    assert lib.vsa_fwd_splits(1920, 128, 1100, 0) == 1
+    assert lib.vsa_fwd_splits(1920, 128, 1100, 4) == 1
+    assert lib.vsa_fwd_splits(1920, 128, 192, 1) == 1
+    assert lib.vsa_fwd_splits(8, 64, 3, 3) == 3
+    assert lib.vsa_fwd_splits(8, 64, 3, 16) == 16
+    assert lib.vsa_fwd_splits(8, 64, 3, 17) == 0
+    assert lib.vsa_fwd_splits(8, 64, 9, 0) == 0
+    # 3 splits of 16 units: lists of 2 * 3 + 4 + 3 * 5 tiles (a zero quarter
+    # and 4 zero tiles per split) x 8 bytes = 3200 -> 3328, first tiles
+    # (16 x 4 int32 = 256), ranks and keys (256 + 256), |v| maxima (512),
+    # exponents (256), partial O (16 x 3 x 64 x 64 float32) and partial row
+    # states (16 x 3 x 64 float4)
+    need = 8 * 64 * 2 * 64 * 2 + 3328 + 256 + 256 + 256 + 512 + 256 + 16 * 3 * 64 * 64 * 4 + \
+        16 * 3 * 64 * 16
+    assert lib.vsa_fwd_workspace_bytes_ex(1, 8, 8, 2, 64, 3, 3) == need
+    assert lib.vsa_fwd_workspace_bytes_ex(1, 8, 8, 2, 64, 3, 0) == \
+        lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 3)
+    assert lib.vsa_fwd_workspace_bytes_ex(1, 8, 8, 2, 64, 3, 17) == 0
+
+    def lut(splits, wsb=need):
+        return lib.vsa_fwd_lut_ex(P, P, P, P, None, P, P, None, None, 1, 8, 8, 2, 64, 3, 0.0,
+                                  splits, P, wsb, None)
+
+    assert lut(-1) == _lib.VSA_ERR_RANGE
+    assert lut(17) == _lib.VSA_ERR_RANGE
+    assert lut(3, need - 1) == _lib.VSA_ERR_WORKSPACE
 
 
 def test_select_noalloc_validation():

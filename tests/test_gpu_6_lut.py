@@ -58,13 +58,14 @@ def _stat_tolerances(q64, k64, idx, valid, vbs, scale):
     return tol_lse
 
 
-def _check(q, k, v, vbs, idx, valid, label, sm_scale=None):
+def _check(q, k, v, vbs, idx, valid, label, sm_scale=None, kv_splits=0):
     B, S, NH, D = q.shape
-    print(f"[{label}] B={B} Nq={S // 64} Nkv={vbs.size} NH={NH} D={D} max_kv={idx.shape[-1]}",
-          flush=True)
+    print(f"[{label}] B={B} Nq={S // 64} Nkv={vbs.size} NH={NH} D={D} max_kv={idx.shape[-1]} "
+          f"splits={vsa.fwd_splits(vbs.size, D, idx.shape[-1], kv_splits)}", flush=True)
     out_t, lse_t, mp_t = vsa.fwd_lut(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v),
                                      torch.from_numpy(idx).cuda(), torch.from_numpy(valid).cuda(),
-                                     torch.from_numpy(vbs).cuda(), sm_scale=sm_scale, stats=True)
+                                     torch.from_numpy(vbs).cuda(), sm_scale=sm_scale, stats=True,
+                                     kv_splits=kv_splits)
     out = from_gpu_bf16(out_t)
     lse, mp = lse_t.cpu().numpy().astype(np.float64), mp_t.cpu().numpy().astype(np.float64)
     q64, k64, v64 = (oracle.decode_bf16(a) for a in (q, k, v))

@@ -51,10 +51,16 @@ SIGNATURES = {
     "vsa_select_cdf": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                                 ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, _sz, _vp]),
     "vsa_fwd_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "vsa_fwd_workspace_bytes_ex": (_sz, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _c_int]),
+    "vsa_fwd_splits": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
     "vsa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
                          _c_int, ctypes.c_float, _vp, _sz, _vp]),
     "vsa_fwd_lut": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
                              _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _vp, _sz, _vp]),
+    "vsa_fwd_lut_ex": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                _c_int, _c_int, _c_int, _c_int, ctypes.c_float, _c_int, _vp, _sz,
+                                _vp]),
     "vsa_coarse_workspace_bytes": (_sz, [_c_int, _c_int, _c_int, _c_int]),
     "vsa_coarse": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp,
                             ctypes.c_float, _vp, _vp, _sz, _vp]),

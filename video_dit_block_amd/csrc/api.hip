@@ -28,7 +28,7 @@ int32_t ok() {
 
 constexpr int64_t kMaxGridX = 2147483647;
 constexpr int64_t kMaxGridYZ = 65535;
-// vsa_fwd addresses a half-tile by a 32-bit byte offset from its head's first
+// vsa_fwd addresses a 16-row tile quarter by a 32-bit byte offset from its head's first
 // key row: one batch's k (Nkv * 64 rows of NH * D bf16) must span < 4 GiB.
 constexpr uint64_t kMaxFwdKvBytes = 1ull << 32;
 
@@ -414,10 +414,24 @@ int32_t vsa_gate_combine(const vsa_bf16_t* o_fine, const float* o_coarse,
                   "gate_combine");
 }
 
+size_t vsa_fwd_workspace_bytes_ex(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                                  int32_t topk, int32_t kv_splits) {
+  if (B <= 0 || Nq <= 0 || Nkv <= 0 || NH <= 0 || D <= 0 || topk <= 0 || kv_splits < 0 ||
+      kv_splits > vsa::kMaxSplits)
+    return 0;
+  return vsa::fwd_workspace(B, Nq, Nkv, NH, D, topk, kv_splits).total;
+}
+
 size_t vsa_fwd_workspace_bytes(int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
                                int32_t topk) {
-  if (B <= 0 || Nq <= 0 || Nkv <= 0 || NH <= 0 || D <= 0 || topk <= 0) return 0;
-  return vsa::fwd_workspace(B, Nq, Nkv, NH, D, topk).total;
+  return vsa_fwd_workspace_bytes_ex(B, Nq, Nkv, NH, D, topk, 0);
+}
+
+int32_t vsa_fwd_splits(int32_t Nkv, int32_t D, int32_t topk, int32_t kv_splits) {
+  if (Nkv <= 0 || D <= 0 || topk <= 0 || topk > Nkv || kv_splits < 0 ||
+      kv_splits > vsa::kMaxSplits)
+    return 0;
+  return vsa::fwd_splits(Nkv, D, topk, kv_splits);
 }
 
 namespace {
@@ -426,15 +440,19 @@ int32_t fwd_common(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v
                    const int32_t* idx, const int32_t* valid, const int32_t* vbs,
                    vsa_bf16_t* out, float* lse, float* max_prob, int32_t B, int32_t Nq,
                    int32_t Nkv, int32_t NH, int32_t D, int32_t row_len, float sm_scale,
-                   void* workspace, size_t workspace_bytes, vsa_stream_t stream) {
+                   int32_t kv_splits, void* workspace, size_t workspace_bytes,
+                   vsa_stream_t stream) {
   int32_t s = check_bhd(B, NH, D);
   if (s != VSA_OK) return s;
   if (Nq <= 0 || Nkv <= 0) return fail(VSA_ERR_SHAPE, "Nq=%d Nkv=%d must be positive", Nq, Nkv);
-  if ((int64_t)B * NH * Nq > kMaxGridX)
-    return fail(VSA_ERR_SHAPE, "B*NH*Nq=%lld exceeds %lld", (long long)B * NH * Nq,
-                (long long)kMaxGridX);
   if (row_len < 1 || row_len > Nkv)
     return fail(VSA_ERR_RANGE, "index row length %d outside [1, %d]", row_len, Nkv);
+  if (kv_splits < 0 || kv_splits > vsa::kMaxSplits)
+    return fail(VSA_ERR_RANGE, "kv_splits=%d outside [0, %d]", kv_splits, vsa::kMaxSplits);
+  const int splits = vsa::fwd_splits(Nkv, D, row_len, kv_splits);
+  if ((int64_t)B * NH * Nq * splits > kMaxGridX)
+    return fail(VSA_ERR_SHAPE, "B*NH*Nq*splits=%lld exceeds %lld",
+                (long long)B * NH * Nq * splits, (long long)kMaxGridX);
   if (!isfinite(sm_scale)) return fail(VSA_ERR_RANGE, "sm_scale is not finite");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(VSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
@@ -442,7 +460,7 @@ int32_t fwd_common(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v
   if ((uint64_t)Nkv * 64u * (uint64_t)NH * (uint64_t)D * 2u >= kMaxFwdKvBytes)
     return fail(VSA_ERR_UNSUPPORTED, "Nkv * 64 * NH * D * 2 = %llu bytes per batch must be < 2^32",
                 (unsigned long long)Nkv * 64ull * NH * D * 2ull);
-  const size_t need = vsa::fwd_workspace(B, Nq, Nkv, NH, D, row_len).total;
+  const size_t need = vsa::fwd_workspace(B, Nq, Nkv, NH, D, row_len, kv_splits).total;
   if (workspace == nullptr || workspace_bytes < need)
     return fail(VSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -451,7 +469,7 @@ int32_t fwd_common(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v
   if (sm_scale <= 0.0f) sm_scale = 1.0f / sqrtf((float)D);
   if ((s = check_device()) != VSA_OK) return s;
   return launched(vsa::launch_fwd(q, k, v, idx, valid, vbs, out, lse, max_prob, B, Nq, Nkv, NH,
-                                  D, row_len, sm_scale, workspace,
+                                  D, row_len, sm_scale, kv_splits, workspace,
                                   static_cast<hipStream_t>(stream)),
                   "fwd");
 }
@@ -467,15 +485,15 @@ int32_t vsa_fwd(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
     return fail(VSA_ERR_NULL, "q, k, v, topk_idx, vbs or out is NULL");
   if (topk < 1 || topk > Nkv) return fail(VSA_ERR_RANGE, "topk=%d outside [1, %d]", topk, Nkv);
   return fwd_common(q, k, v, topk_idx, nullptr, vbs, out, nullptr, nullptr, B, Nq, Nkv, NH, D,
-                    topk, sm_scale, workspace, workspace_bytes, stream);
+                    topk, sm_scale, 0, workspace, workspace_bytes, stream);
 }
 
-int32_t vsa_fwd_lut(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
-                    const int32_t* kv_block_idx, const int32_t* valid_block_num,
-                    const int32_t* vbs, vsa_bf16_t* out, float* lse, float* max_prob,
-                    int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
-                    int32_t max_kv, float sm_scale, void* workspace,
-                    size_t workspace_bytes, vsa_stream_t stream) {
+int32_t vsa_fwd_lut_ex(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                       const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                       const int32_t* vbs, vsa_bf16_t* out, float* lse, float* max_prob,
+                       int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                       int32_t max_kv, float sm_scale, int32_t kv_splits, void* workspace,
+                       size_t workspace_bytes, vsa_stream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || kv_block_idx == nullptr ||
       vbs == nullptr || out == nullptr)
     return fail(VSA_ERR_NULL, "q, k, v, kv_block_idx, vbs or out is NULL");
@@ -485,7 +503,17 @@ int32_t vsa_fwd_lut(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* 
       (max_prob != nullptr && (reinterpret_cast<uintptr_t>(max_prob) & 3u) != 0))
     return fail(VSA_ERR_UNSUPPORTED, "lse and max_prob must be 4-byte aligned");
   return fwd_common(q, k, v, kv_block_idx, valid_block_num, vbs, out, lse, max_prob, B, Nq,
-                    Nkv, NH, D, max_kv, sm_scale, workspace, workspace_bytes, stream);
+                    Nkv, NH, D, max_kv, sm_scale, kv_splits, workspace, workspace_bytes, stream);
+}
+
+int32_t vsa_fwd_lut(const vsa_bf16_t* q, const vsa_bf16_t* k, const vsa_bf16_t* v,
+                    const int32_t* kv_block_idx, const int32_t* valid_block_num,
+                    const int32_t* vbs, vsa_bf16_t* out, float* lse, float* max_prob,
+                    int32_t B, int32_t Nq, int32_t Nkv, int32_t NH, int32_t D,
+                    int32_t max_kv, float sm_scale, void* workspace,
+                    size_t workspace_bytes, vsa_stream_t stream) {
+  return vsa_fwd_lut_ex(q, k, v, kv_block_idx, valid_block_num, vbs, out, lse, max_prob, B, Nq,
+                        Nkv, NH, D, max_kv, sm_scale, 0, workspace, workspace_bytes, stream);
 }
 
 int32_t vsa_validate_topk(const int32_t* topk_idx, int32_t B, int32_t NH, int32_t Nq,

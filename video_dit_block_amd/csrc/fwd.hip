@@ -63,10 +63,10 @@
 //   exceeds it by more than 2^8 (log2 units: 8) does the wave rescale O and l
 //   by exp2((m_old - m_new) c); otherwise p may reach 2^8 * 2^7, which fp32
 //   and fp16 hold in range. The constant 2^7 keeps weights down to 2^-21 of
-//   the reference max normal in fp16; it cancels in O / l. Tokens past a quarter's real rows are set to -inf
-//   in registers before the max (tiles with a partial quarter only). O^T
-//   accumulates in fp32, each lane holding D/2 values of its own query row,
-//   so the rescale is a per-lane multiply.
+//   the reference max normal in fp16; it cancels in O / l. Tokens past a
+//   quarter's real rows are set to -inf in registers before the max (tiles
+//   with a partial quarter only). O^T accumulates in fp32, each lane holding
+//   D/2 values of its own query row, so the rescale is a per-lane multiply.
 // * Precision: QK^T is a bf16 MFMA with fp32 accumulation. The PV product
 //   runs as an fp16 MFMA (v_mfma_f32_32x32x16_f16): P is rounded to fp16 and
 //   V is converted to fp16 by the pre-pass. fp16 keeps 3 more significand
@@ -358,15 +358,26 @@ __global__ __launch_bounds__(kCvtThreads) void vfix_kernel(
 // Tile t = quarters 2t and 2t+1; an odd last quarter is paired with 0 (no
 // rows), and kListPad all-zero tiles follow the last one. Rows with
 // topk > kListSortCap keep the given order.
+//
+// With key-range splits (splits > 1, sorted rows only), the quarters of the
+// cubes of split s (ids j with j * splits / Nkv == s) form tiles of their
+// own: a split whose quarter count is odd ends with a zero quarter, so that
+// no tile mixes two splits, and kListPad zero tiles follow every split.
+// sbeg[unit][s] is the first tile of split s (of the list: s = 0) and
+// sbeg[unit][splits] the end of the list, so split s has
+// sbeg[s + 1] - sbeg[s] - kListPad tiles.
 constexpr int kListSortCap = 1024;
 constexpr int kListPad = 4;
 constexpr int kQuarter = 16;  // rows per quarter
 
 __global__ __launch_bounds__(64) void tiles_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ valid,
-    const int32_t* __restrict__ vbs, uint32_t* __restrict__ list, int32_t* __restrict__ counts,
-    int Nkv, int row_len, int stride, uint32_t rs2) {
+    const int32_t* __restrict__ vbs, uint32_t* __restrict__ list, int32_t* __restrict__ sbeg,
+    int Nkv, int row_len, int stride, uint32_t rs2, int splits) {
   __shared__ int32_t keys[kListSortCap];
+  __shared__ int32_t qcount[kMaxSplits];  // quarters of split s
+  __shared__ int32_t qpad[kMaxSplits];    // zero quarters placed before split s
+  __shared__ int32_t qend[kMaxSplits];    // first quarter after split s's tiles
   const int unit = blockIdx.x, lane = threadIdx.x;
   const int32_t* __restrict__ sel = topk_idx + (size_t)unit * row_len;
   // the row's first `topk` ids are used: all of them, or valid[unit] (clamped)
@@ -394,8 +405,39 @@ __global__ __launch_bounds__(64) void tiles_kernel(
       }
     __syncthreads();
   }
+  int32_t* __restrict__ sb = sbeg + (size_t)unit * (splits + 1);
+  auto split_of = [&](int id) __attribute__((always_inline)) -> int {
+    return (int)(((int64_t)id * splits) / Nkv);
+  };
+  if (splits > 1) {  // the host allows splits only for sorted rows
+    if (lane < kMaxSplits) qcount[lane] = 0;
+    __syncthreads();
+    for (int i = lane; i < topk; i += 64) {
+      const int id = keys[i];
+      const int nv = min(max(vbs[id], 0), kCube);
+      atomicAdd(&qcount[split_of(id)], (nv + kQuarter - 1) / kQuarter);
+    }
+    __syncthreads();
+    if (lane == 0) {
+      int pad = 0, start = 0;  // start: first quarter of split s
+      for (int sp = 0; sp < splits; ++sp) {
+        const int qn = qcount[sp];
+        qpad[sp] = pad;
+        sb[sp] = start / 2;
+        qend[sp] = start + qn + (qn & 1);
+        pad += (qn & 1) + 2 * kListPad;
+        start = qend[sp] + 2 * kListPad;
+      }
+      sb[splits] = start / 2;
+    }
+    __syncthreads();
+    // an odd split's completing zero quarter, then the split's zero tiles
+    for (int sp = 0; sp < splits; ++sp)
+      if (lane < 2 * kListPad + 1 && (lane > 0 || (qcount[sp] & 1)))
+        out[qend[sp] - 1 + lane] = 0u;
+  }
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  int base = 0;  // quarters written so far
+  int base = 0;  // quarters written so far, without the zero quarters
   for (int c0 = 0; c0 < topk; c0 += 64) {
     const int i = c0 + lane;
     int id = 0, nv = 0;
@@ -404,7 +446,7 @@ __global__ __launch_bounds__(64) void tiles_kernel(
       nv = min(max(vbs[id], 0), kCube);
     }
     const int nq = (nv + kQuarter - 1) / kQuarter;  // 0..4
-    int pos = base, tot = 0;
+    int pos = base + (splits > 1 && i < topk ? qpad[split_of(id)] : 0), tot = 0;
 #pragma unroll
     for (int k = 1; k <= kCube / kQuarter; ++k) {
       const uint64_t bk = __builtin_amdgcn_ballot_w64(nq >= k);
@@ -416,10 +458,14 @@ __global__ __launch_bounds__(64) void tiles_kernel(
       out[pos + k] = (off0 + (uint32_t)(kQuarter * k) * rs2) | (uint32_t)min(nv - kQuarter * k, kQuarter);
     base += tot;
   }
+  if (splits > 1) return;
   const int n_tiles = (base + 1) / 2;
   if (lane == 0 && (base & 1)) out[base] = 0u;
   if (lane < 2 * kListPad) out[2 * n_tiles + lane] = 0u;
-  if (lane == 0) counts[unit] = n_tiles;
+  if (lane == 0) {
+    sb[0] = 0;
+    sb[1] = n_tiles + kListPad;
+  }
 }
 
 // Dispatch order inside each (b, h): query cubes by descending count of
@@ -477,19 +523,21 @@ template <int D, bool kStats>
 __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v16, const uint32_t* __restrict__ list,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ sbeg, const int32_t* __restrict__ order,
     const int32_t* __restrict__ vexp, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ max_prob, int Nq, int Nkv, int NH, int list_stride, float scale_log2,
-    int n_units) {
+    float* __restrict__ max_prob, float* __restrict__ part, float4* __restrict__ pstat,
+    int Nq, int Nkv, int NH, int list_stride, float scale_log2, int splits, int n_items) {
   using S = FwdShape<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][S::kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][S::kTileBytes];
 
-  // XCD x runs a contiguous range of (b, h, rank); within a (b, h) the query
-  // cube of a rank is the rank itself, or order[] for per-row counts
-  const int lin = xcd_remap(blockIdx.x, n_units);
-  const int bh = lin / Nq;
-  const int qc = order == nullptr ? lin - bh * Nq : min(max(order[lin], 0), Nq - 1);
+  // XCD x runs a contiguous range of (b, h, split, rank); within a (b, h)
+  // the query cube of a rank is the rank itself, or order[]
+  const int lin = xcd_remap(blockIdx.x, n_items);
+  const int bh = lin / (Nq * splits);
+  const int rem = lin - bh * Nq * splits;
+  const int sp = rem / Nq, rank = rem - sp * Nq;
+  const int qc = order == nullptr ? rank : min(max(order[bh * Nq + rank], 0), Nq - 1);
   const int unit = bh * Nq + qc;
   const int h = bh % NH, b = bh / NH;
   const size_t row_stride = (size_t)NH * D;  // elements between tokens
@@ -509,10 +557,13 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   }
   uint16_t* const orow = out + qrow * row_stride + (size_t)h * D;
 
-  // ---- the unit's tiles (two quarters each); reads past the list (i >= n)
-  // see the all-zero padding tiles (i < n + kListPad)
-  const uint32_t* __restrict__ lst = list + (size_t)unit * list_stride * 2;
-  const int n = __builtin_amdgcn_readfirstlane(counts[unit]);
+  // ---- the tiles (two quarters each) of this unit's split: n tiles from
+  // tile t0 of the unit's list; reads past them (i >= n) see the split's
+  // all-zero padding tiles (i < n + kListPad), whose loads fetch nothing
+  const int32_t* __restrict__ sb = sbeg + (size_t)unit * (splits + 1) + sp;
+  const int t0 = __builtin_amdgcn_readfirstlane(sb[0]);
+  const int n = __builtin_amdgcn_readfirstlane(sb[1]) - t0 - kListPad;
+  const uint32_t* __restrict__ lst = list + (size_t)unit * list_stride * 2 + 2 * (size_t)t0;
   auto ent = [&](int i) __attribute__((always_inline)) -> u32x2 {
     const u32x2 v = *reinterpret_cast<const u32x2*>(lst + 2 * __builtin_amdgcn_readfirstlane(i));
     return u32x2{(uint32_t)__builtin_amdgcn_readfirstlane((int)v[0]),
@@ -521,6 +572,7 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
   // per-row statistics: row (b, h, c * 64 + 32 wave + qr), written by lane g = 0
   const size_t srow = ((size_t)bh * Nq + qc) * kCube + 32 * wave + qr;
   if (n == 0) {  // no real key in any selected cube: the rows are 0
+    if (splits > 1) return;  // the merge skips empty splits
 #pragma unroll
     for (int db = 0; db < S::kDBlocks; ++db)
 #pragma unroll
@@ -784,6 +836,23 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
       pv(0, pb, none, -1);
   }
 
+  // ---- with key-range splits: the partial result of this split, O
+  // unnormalised (fp32, [item][row][D]) and (m_ref, l_run, m_row) per row
+  if (splits > 1) {
+    const size_t item = (size_t)unit * splits + sp;
+    const int row = 32 * wave + qr;
+    float* __restrict__ po = part + (item * kCube + row) * D;
+#pragma unroll
+    for (int db = 0; db < S::kDBlocks; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * r4 + 4 * g) =
+            float4{oacc[db][4 * r4], oacc[db][4 * r4 + 1], oacc[db][4 * r4 + 2],
+                   oacc[db][4 * r4 + 3]};
+    if (g == 0) pstat[item * kCube + row] = float4{m_ref, l_run, m_row, 0.0f};
+    return;
+  }
+
   // ---- per-row statistics. l_run sums exp2((s - m_ref) c + kPShift), so the
   // natural log-sum-exp of the scaled scores is (m_ref c - kPShift +
   // log2 l_run) ln 2, and the largest softmax weight is
@@ -807,35 +876,134 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of the key-range splits: one workgroup per unit (b, h, query cube),
+// four threads per query row, each combining D/4 columns. With M the largest
+// reference max over the row's non-empty splits and w_s = exp2((m_s - M) c),
+// O = sum_s w_s O_s and l = sum_s w_s l_s (the online-softmax combination of
+// partial states), out = O / l * 2^e_h rounded to bf16, and the statistics
+// are the unsplit epilogue's with (M, l) and the largest row max.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(
+    const float* __restrict__ part, const float4* __restrict__ pstat,
+    const int32_t* __restrict__ sbeg, const int32_t* __restrict__ vexp,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ max_prob, int Nq,
+    int NH, int splits, float scale_log2) {
+  constexpr int kCols = D / 4;
+  const int unit = blockIdx.x;
+  const int bh = unit / Nq, qc = unit - bh * Nq, h = bh % NH, b = bh / NH;
+  const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * kCols;
+  const int32_t* __restrict__ sb = sbeg + (size_t)unit * (splits + 1);
+  float M = kNegInf, m_row = kNegInf;
+  for (int sp = 0; sp < splits; ++sp) {
+    if (sb[sp + 1] - sb[sp] == kListPad) continue;  // an empty split
+    const float4 st = pstat[((size_t)unit * splits + sp) * kCube + row];
+    M = fmaxf(M, st.x);
+    m_row = fmaxf(m_row, st.z);
+  }
+  float acc[kCols];
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) acc[i] = 0.0f;
+  float l = 0.0f;
+  for (int sp = 0; sp < splits; ++sp) {
+    if (sb[sp + 1] - sb[sp] == kListPad) continue;
+    const size_t item = (size_t)unit * splits + sp;
+    const float4 st = pstat[item * kCube + row];
+    const float w = __builtin_amdgcn_exp2f((st.x - M) * scale_log2);
+    l = __builtin_fmaf(w, st.y, l);
+    const float4* __restrict__ po =
+        reinterpret_cast<const float4*>(part + (item * kCube + row) * D + c0);
+#pragma unroll
+    for (int i = 0; i < kCols / 4; ++i) {
+      const float4 x = po[i];
+      acc[4 * i] = __builtin_fmaf(w, x.x, acc[4 * i]);
+      acc[4 * i + 1] = __builtin_fmaf(w, x.y, acc[4 * i + 1]);
+      acc[4 * i + 2] = __builtin_fmaf(w, x.z, acc[4 * i + 2]);
+      acc[4 * i + 3] = __builtin_fmaf(w, x.w, acc[4 * i + 3]);
+    }
+  }
+  const size_t srow = (size_t)unit * kCube + row;
+  if ((threadIdx.x & 3) == 0) {
+    if (lse != nullptr)
+      lse[srow] = l > 0.0f ? (M * scale_log2 - kPShift + __log2f(l)) * 0.69314718055994531f
+                           : kNegInf;
+    if (max_prob != nullptr)
+      max_prob[srow] =
+          l > 0.0f ? __builtin_amdgcn_exp2f((m_row - M) * scale_log2 + kPShift) / l : 0.0f;
+  }
+  const int ve = vexp == nullptr ? 0 : vexp[bh];
+  const float inv_l = l > 0.0f ? ldexpf(1.0f / l, ve) : 0.0f;
+  uint16_t* __restrict__ orow =
+      out + (((size_t)b * Nq + qc) * kCube + row) * (size_t)NH * D + (size_t)h * D + c0;
+#pragma unroll
+  for (int i = 0; i < kCols / 8; ++i) {
+    const u32x4 w4 = {pack_bf16x2(acc[8 * i] * inv_l, acc[8 * i + 1] * inv_l),
+                      pack_bf16x2(acc[8 * i + 2] * inv_l, acc[8 * i + 3] * inv_l),
+                      pack_bf16x2(acc[8 * i + 4] * inv_l, acc[8 * i + 5] * inv_l),
+                      pack_bf16x2(acc[8 * i + 6] * inv_l, acc[8 * i + 7] * inv_l)};
+    *reinterpret_cast<u32x4*>(orow + 8 * i) = w4;
+  }
+}
+
 }  // namespace
 
-FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk) {
+// Key-range splits of the fine stage (split-KV). The units of a head that
+// run side by side on an XCD sweep that head's keys; once one head's K and
+// fp16 V exceed about 32 MiB (a few times the XCD's 4 MiB L2) their tiles are
+// evicted before the other units reach them, and the kernel fetches many
+// times its algorithmic bytes from beyond L2 (measured at the 720p shape:
+// 65x, 29% L2 hits, 7.3 TB/s). Split into S key ranges of about 16 MiB, run
+// split-major inside each head, the resident units share one range; each
+// item leaves a partial state that merge_kernel combines. forced: 0 chooses,
+// 1 turns splitting off, 2..kMaxSplits forces S. Rows longer than the sorted
+// list pre-pass allows (kListSortCap ids) are never split.
+int fwd_splits(int Nkv, int D, int topk, int forced) {
+  if (topk > kListSortCap) return 1;
+  if (forced > 0) return forced < kMaxSplits ? forced : kMaxSplits;
+  const double kv_head = (double)Nkv * kCube * D * 4.0;  // K bf16 + V fp16
+  const double mib = 1024.0 * 1024.0;
+  if (kv_head <= 32.0 * mib) return 1;
+  int sp = (int)ceil(kv_head / (16.0 * mib));
+  sp = sp < topk / 8 ? sp : topk / 8;  // at least 8 selected cubes per item on average
+  return sp < 2 ? 1 : (sp < kMaxSplits ? sp : kMaxSplits);
+}
+
+FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk, int forced) {
   auto up = [](size_t n) { return (n + 255) & ~(size_t)255; };
   FwdWorkspace w;
-  // tiles per unit: at most 4 quarters per cube, two per tile
-  w.list_stride = 2 * topk + kListPad;  // tiles per unit, 8 bytes each
+  w.splits = fwd_splits(Nkv, D, topk, forced);
+  // tiles per unit: at most 4 quarters per cube, two per tile, then
+  // kListPad zero tiles; with splits a zero quarter and kListPad zero tiles
+  // per split
+  w.list_stride = 2 * topk + kListPad + (w.splits > 1 ? w.splits * (kListPad + 1) : 0);
   const size_t units = (size_t)B * NH * Nq;
   w.v16_off = 0;
   w.list_off = up((size_t)B * Nkv * kCube * NH * D * 2);
-  w.count_off = w.list_off + up(units * w.list_stride * 8);
-  w.order_off = w.count_off + up(units * 4);
+  w.sbeg_off = w.list_off + up(units * w.list_stride * 8);
+  w.order_off = w.sbeg_off + up(units * (w.splits + 1) * 4);
   w.key_off = w.order_off + up(units * 4);
   w.vmax_off = w.key_off + up(units * 8);
   w.vexp_off = w.vmax_off + up((size_t)B * Nkv * kCvtSplit * NH * 4);
-  w.total = w.vexp_off + up((size_t)B * NH * 4);
+  w.part_off = w.vexp_off + up((size_t)B * NH * 4);
+  const size_t items = w.splits > 1 ? units * w.splits : 0;
+  w.pstat_off = w.part_off + up(items * kCube * D * 4);
+  w.total = w.pstat_off + up(items * kCube * 16);
   return w;
 }
 
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* topk_idx, const int32_t* valid, const int32_t* vbs,
                       uint16_t* out, float* lse, float* max_prob, int B, int Nq, int Nkv,
-                      int NH, int D, int topk, float sm_scale, void* workspace,
-                      hipStream_t stream) {
-  const FwdWorkspace w = fwd_workspace(B, Nq, Nkv, NH, D, topk);
+                      int NH, int D, int topk, float sm_scale, int forced_splits,
+                      void* workspace, hipStream_t stream) {
+  const FwdWorkspace w = fwd_workspace(B, Nq, Nkv, NH, D, topk, forced_splits);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(ws + w.v16_off);
   uint32_t* list = reinterpret_cast<uint32_t*>(ws + w.list_off);
-  int32_t* counts = reinterpret_cast<int32_t*>(ws + w.count_off);
+  int32_t* sbeg = reinterpret_cast<int32_t*>(ws + w.sbeg_off);
+  float* part = reinterpret_cast<float*>(ws + w.part_off);
+  float4* pstat = reinterpret_cast<float4*>(ws + w.pstat_off);
+  const int splits = w.splits;
   uint32_t* vmax = reinterpret_cast<uint32_t*>(ws + w.vmax_off);
   int32_t* vexp = reinterpret_cast<int32_t*>(ws + w.vexp_off);
   int32_t* order = nullptr;
@@ -872,15 +1040,16 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(tiles_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, valid, vbs,
-                     list, counts, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u);
+                     list, sbeg, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u, splits);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   const bool stats = lse != nullptr || max_prob != nullptr;
-#define VSA_FWD_LAUNCH(DD, ST)                                                                 \
-  hipLaunchKernelGGL((fwd_kernel<DD, ST>), dim3(n_units), dim3(FwdShape<DD>::kThreads), 0, stream, \
-                     q, k, v16, list, counts, order, vexp, out, lse, max_prob, Nq, Nkv, NH,     \
-                     w.list_stride, scale_log2, n_units)
+  const int n_items = n_units * splits;
+#define VSA_FWD_LAUNCH(DD, ST)                                                                  \
+  hipLaunchKernelGGL((fwd_kernel<DD, ST>), dim3(n_items), dim3(FwdShape<DD>::kThreads), 0, stream, \
+                     q, k, v16, list, sbeg, order, vexp, out, lse, max_prob, part, pstat, Nq,    \
+                     Nkv, NH, w.list_stride, scale_log2, splits, n_items)
   if (D == 128) {
     if (stats) VSA_FWD_LAUNCH(128, true);
     else VSA_FWD_LAUNCH(128, false);
@@ -889,6 +1058,14 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     else VSA_FWD_LAUNCH(64, false);
   }
 #undef VSA_FWD_LAUNCH
+  e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  if (D == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(n_units), dim3(256), 0, stream, part, pstat, sbeg,
+                       vexp, out, lse, max_prob, Nq, NH, splits, scale_log2);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(n_units), dim3(256), 0, stream, part, pstat, sbeg,
+                       vexp, out, lse, max_prob, Nq, NH, splits, scale_log2);
   return hipGetLastError();
 }
 

@@ -66,22 +66,32 @@ hipError_t launch_select(const uint16_t* q_tiled, const uint16_t* k_tiled,
                          int topk, int32_t* topk_idx, int32_t* valid, float scale, float tau,
                          void* workspace, hipStream_t stream, int row_nh = 0);
 
+// Key-range splits of the fine stage: at most kMaxSplits; fwd_splits gives
+// the number used (forced: 0 = chosen from the sizes, 1 = none, 2.. = that
+// many; rows of more than 1024 ids are never split).
+constexpr int kMaxSplits = 16;
+int fwd_splits(int Nkv, int D, int topk, int forced);
+
 // Workspace carve-up of vsa_fwd: an fp16 copy of v in the tiled layout, the
 // tile lists of the units ([B*NH*Nq][list_stride] pairs of uint32 quarters),
-// their lengths, the dispatch order and its sort keys, the per-(workgroup,
-// head) maxima of |v| and the per-(b, h) exponent of v's fp16 copy.
+// the first tile of every split of a unit ([B*NH*Nq][splits + 1]), the
+// dispatch order and its sort keys, the per-(workgroup, head) maxima of |v|,
+// the per-(b, h) exponent of v's fp16 copy, and with splits the partial
+// results: O as fp32 [B*NH*Nq*splits][64][D] and (m, l, row max, 0) as
+// float4 [B*NH*Nq*splits][64].
 struct FwdWorkspace {
-  size_t v16_off, list_off, count_off, order_off, key_off, vmax_off, vexp_off, total;
-  int list_stride;
+  size_t v16_off, list_off, sbeg_off, order_off, key_off, vmax_off, vexp_off, part_off,
+      pstat_off, total;
+  int list_stride, splits;
 };
-FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk);
+FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk, int forced = 0);
 // topk_idx rows hold `topk` ids; valid (may be NULL = all) gives the count
 // used per row; lse and max_prob (may be NULL) receive per-row statistics.
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* topk_idx, const int32_t* valid, const int32_t* vbs,
                       uint16_t* out, float* lse, float* max_prob, int B, int Nq, int Nkv,
-                      int NH, int D, int topk, float sm_scale, void* workspace,
-                      hipStream_t stream);
+                      int NH, int D, int topk, float sm_scale, int forced_splits,
+                      void* workspace, hipStream_t stream);
 
 hipError_t launch_validate_topk(const int32_t* topk_idx, int B, int NH, int Nq,
                                 int Nkv, int topk, int32_t* bad_count,

@@ -7,7 +7,9 @@
 // datasheet figure. (2) An engine-clock meter: small workgroups that wait on the
 // 100 MHz real-time counter (s_memrealtime) for a fixed span while reading the
 // shader cycle counter (s_memtime), launched on a second stream beside a timed
-// loop; the ratio of the two counts is the clock the loop ran at. Built into
+// loop; the ratio of the two counts is the clock the loop ran at. (3) An LDS
+// read pattern with and without bank conflicts, a control for the profiler's
+// bank-conflict counter. Built into
 // its own library (libvsa_probe.so), loaded only by the benchmark.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -70,9 +72,53 @@ __global__ __launch_bounds__(64) void clock_meter_kernel(uint64_t ticks,
   }
 }
 
+// LDS bank-conflict control for the profiler's conflict counter: every lane
+// reads `width` bytes at byte (lane * stride * width + 4 * (it & 7)) of a
+// 32 KiB LDS array, `iters` times. stride 1 gives contiguous, conflict-free
+// reads; stride 8 puts the lanes of a read on few banks. All addresses stay
+// below 64 * 8 * 16 + 28 bytes.
+template <int kWidth>
+__global__ __launch_bounds__(64) void lds_conflict_kernel(int stride, int iters,
+                                                          float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) float lds[8192];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < 8192; i += 64) lds[i] = (float)(i & 255);
+  __syncthreads();
+  float acc = 0.0f;
+  const int base = lane * stride * (kWidth / 4);
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" ::: "memory");  // one LDS read per iteration, none hoisted
+    const int w = base + (it & 7);
+    if (kWidth == 16) {
+      const float4 x = *reinterpret_cast<const float4*>(&lds[w & ~3]);
+      acc += x.x + x.y + x.z + x.w;
+    } else {
+      acc += lds[w];
+    }
+  }
+  out[(size_t)blockIdx.x * 64 + lane] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Launches `blocks` one-wave workgroups of the LDS conflict control on
+// `stream`; width 4 or 16 bytes, stride 1..8; out: device float buffer of
+// blocks * 64 entries.
+int32_t vsa_probe_lds(int32_t width, int32_t stride, int32_t blocks, int32_t iters, float* out,
+                      void* stream) {
+  if (out == nullptr || (width != 4 && width != 16) || stride < 1 || stride > 8 || blocks <= 0 ||
+      iters <= 0)
+    return (int32_t)hipErrorInvalidValue;
+  if (width == 4)
+    hipLaunchKernelGGL(lds_conflict_kernel<4>, dim3(blocks), dim3(64), 0,
+                       static_cast<hipStream_t>(stream), stride, iters, out);
+  else
+    hipLaunchKernelGGL(lds_conflict_kernel<16>, dim3(blocks), dim3(64), 0,
+                       static_cast<hipStream_t>(stream), stride, iters, out);
+  return (int32_t)hipGetLastError();
+}
 
 // Launches `slots` one-wave workgroups (8: one per XCD, as workgroups are
 // dealt to the XCDs in turn) that each run for `ticks` of the 100 MHz

@@ -219,8 +219,14 @@ def select_cdf(q_t: torch.Tensor, k_t: torch.Tensor, vbs: torch.Tensor, max_k: i
     return idx, valid
 
 
-def fwd_workspace_bytes(B: int, Nq: int, Nkv: int, NH: int, D: int, topk: int) -> int:
-    return int(_lib.load().vsa_fwd_workspace_bytes(B, Nq, Nkv, NH, D, topk))
+def fwd_workspace_bytes(B: int, Nq: int, Nkv: int, NH: int, D: int, topk: int,
+                        kv_splits: int = 0) -> int:
+    return int(_lib.load().vsa_fwd_workspace_bytes_ex(B, Nq, Nkv, NH, D, topk, kv_splits))
+
+
+def fwd_splits(Nkv: int, D: int, topk: int, kv_splits: int = 0) -> int:
+    """Key-range splits the fine stage uses (0 = invalid arguments)."""
+    return int(_lib.load().vsa_fwd_splits(Nkv, D, topk, kv_splits))
 
 
 def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch.Tensor,
@@ -262,11 +268,12 @@ def fwd(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, topk_idx: torch
 def fwd_lut(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
             kv_block_idx: torch.Tensor, valid_block_num: torch.Tensor | None, vbs: torch.Tensor,
             sm_scale: float | None = None, stats: bool = False,
-            workspace: torch.Tensor | None = None):
+            workspace: torch.Tensor | None = None, kv_splits: int = 0):
     """Fine attention over the first valid_block_num[b, h, c] ids of each
     kv_block_idx row (B, NH, Nq, max_kv); valid_block_num (B, NH, Nq) or None
     for all. Returns out, or (out, lse, max_prob) with the per-row statistics
-    (B, NH, Nq*64) float32 when stats is true."""
+    (B, NH, Nq*64) float32 when stats is true. kv_splits: key-range splits
+    (0 = chosen from the sizes, 1 = none, 2..16 = that many)."""
     for t, n in ((q_t, "q_t"), (k_t, "k_t"), (v_t, "v_t")):
         _bf16(t, n)
     _i32(kv_block_idx, "kv_block_idx")
@@ -294,15 +301,17 @@ def fwd_lut(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor,
         mp = torch.empty((B, NH, Sq), dtype=torch.float32, device=q_t.device)
     scale = 0.0 if sm_scale is None else float(sm_scale)
     if workspace is None:
-        workspace = torch.empty(fwd_workspace_bytes(B, Nq, Nkv, NH, D, max_kv),
+        workspace = torch.empty(fwd_workspace_bytes(B, Nq, Nkv, NH, D, max_kv, kv_splits),
                                 dtype=torch.uint8, device=q_t.device)
     ptr = lambda t: None if t is None else t.data_ptr()
-    _lib.check(_lib.load().vsa_fwd_lut(q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(),
-                                       kv_block_idx.data_ptr(), ptr(valid_block_num),
-                                       vbs.data_ptr(), out.data_ptr(), ptr(lse), ptr(mp), B, Nq,
-                                       Nkv, NH, D, max_kv, scale, workspace.data_ptr(),
-                                       workspace.numel() * workspace.element_size(), _stream()),
-               "vsa_fwd_lut")
+    _lib.check(_lib.load().vsa_fwd_lut_ex(q_t.data_ptr(), k_t.data_ptr(), v_t.data_ptr(),
+                                          kv_block_idx.data_ptr(), ptr(valid_block_num),
+                                          vbs.data_ptr(), out.data_ptr(), ptr(lse), ptr(mp), B,
+                                          Nq, Nkv, NH, D, max_kv, scale, int(kv_splits),
+                                          workspace.data_ptr(),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream()),
+               "vsa_fwd_lut_ex")
     return (out, lse, mp) if stats else out
 
 
