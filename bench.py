@@ -395,9 +395,12 @@ def main():
     vbs = torch.empty(Nc, dtype=torch.int32, device=dev)
     ws = torch.empty(vsa.select_workspace_bytes(B, NH, Nc, D), dtype=torch.uint8, device=dev)
     idx = torch.empty((B, NH, Nc, topk), dtype=torch.int32, device=dev)
-    # sized for topk = Nc: covers every topk of the dense run and the sweep
-    wsf = torch.empty(vsa.fwd_workspace_bytes(B, Nc, Nc, NH, D, Nc), dtype=torch.uint8,
-                      device=dev)
+    # one workspace for every fine-stage call of the run: the largest of the
+    # sizes needed by its index-row lengths (with key-range splits the size
+    # is not monotone in the row length)
+    row_lens = {topk, Nc, Nc // 2, *synth.SWEEP_TOPK}
+    wsf = torch.empty(max(vsa.fwd_workspace_bytes(B, Nc, Nc, NH, D, t) for t in row_lens
+                          if t <= Nc), dtype=torch.uint8, device=dev)
     out = torch.empty_like(qt)
     out_nat = torch.empty_like(q)
     ev = lambda: torch.cuda.Event(enable_timing=True)

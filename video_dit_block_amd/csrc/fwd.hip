@@ -882,22 +882,30 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 // reference max over the row's non-empty splits and w_s = exp2((m_s - M) c),
 // O = sum_s w_s O_s and l = sum_s w_s l_s (the online-softmax combination of
 // partial states), out = O / l * 2^e_h rounded to bf16, and the statistics
-// are the unsplit epilogue's with (M, l) and the largest row max.
-template <int D>
+// are the unsplit epilogue's with (M, l) and the largest row max. kS > 0:
+// exactly kS splits, every split's columns loaded before any is combined
+// (the kernel is bound by reading the partial states); kS = 0: any count.
+template <int D, int kS>
 __global__ __launch_bounds__(256) void merge_kernel(
     const float* __restrict__ part, const float4* __restrict__ pstat,
     const int32_t* __restrict__ sbeg, const int32_t* __restrict__ vexp,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ max_prob, int Nq,
     int NH, int splits, float scale_log2) {
   constexpr int kCols = D / 4;
+  constexpr int kVec = kCols / 4;  // float4 per split and thread
   const int unit = blockIdx.x;
   const int bh = unit / Nq, qc = unit - bh * Nq, h = bh % NH, b = bh / NH;
   const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * kCols;
-  const int32_t* __restrict__ sb = sbeg + (size_t)unit * (splits + 1);
+  const int nsp = kS > 0 ? kS : splits;
+  const int32_t* __restrict__ sb = sbeg + (size_t)unit * (nsp + 1);
+  auto part_at = [&](int sp) __attribute__((always_inline)) {
+    return reinterpret_cast<const float4*>(part + (((size_t)unit * nsp + sp) * kCube + row) * D +
+                                           c0);
+  };
   float M = kNegInf, m_row = kNegInf;
-  for (int sp = 0; sp < splits; ++sp) {
+  for (int sp = 0; sp < nsp; ++sp) {
     if (sb[sp + 1] - sb[sp] == kListPad) continue;  // an empty split
-    const float4 st = pstat[((size_t)unit * splits + sp) * kCube + row];
+    const float4 st = pstat[((size_t)unit * nsp + sp) * kCube + row];
     M = fmaxf(M, st.x);
     m_row = fmaxf(m_row, st.z);
   }
@@ -905,21 +913,42 @@ __global__ __launch_bounds__(256) void merge_kernel(
 #pragma unroll
   for (int i = 0; i < kCols; ++i) acc[i] = 0.0f;
   float l = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) {
-    if (sb[sp + 1] - sb[sp] == kListPad) continue;
-    const size_t item = (size_t)unit * splits + sp;
-    const float4 st = pstat[item * kCube + row];
-    const float w = __builtin_amdgcn_exp2f((st.x - M) * scale_log2);
-    l = __builtin_fmaf(w, st.y, l);
-    const float4* __restrict__ po =
-        reinterpret_cast<const float4*>(part + (item * kCube + row) * D + c0);
+  auto combine = [&](float w, const float4 (&x)[kVec]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kCols / 4; ++i) {
-      const float4 x = po[i];
-      acc[4 * i] = __builtin_fmaf(w, x.x, acc[4 * i]);
-      acc[4 * i + 1] = __builtin_fmaf(w, x.y, acc[4 * i + 1]);
-      acc[4 * i + 2] = __builtin_fmaf(w, x.z, acc[4 * i + 2]);
-      acc[4 * i + 3] = __builtin_fmaf(w, x.w, acc[4 * i + 3]);
+    for (int i = 0; i < kVec; ++i) {
+      acc[4 * i] = __builtin_fmaf(w, x[i].x, acc[4 * i]);
+      acc[4 * i + 1] = __builtin_fmaf(w, x[i].y, acc[4 * i + 1]);
+      acc[4 * i + 2] = __builtin_fmaf(w, x[i].z, acc[4 * i + 2]);
+      acc[4 * i + 3] = __builtin_fmaf(w, x[i].w, acc[4 * i + 3]);
+    }
+  };
+  if constexpr (kS > 0) {
+    float4 x[kS][kVec];
+    float w[kS];
+#pragma unroll
+    for (int sp = 0; sp < kS; ++sp) {
+      const bool live = sb[sp + 1] - sb[sp] != kListPad;
+      const float4 st = live ? pstat[((size_t)unit * kS + sp) * kCube + row]
+                             : float4{kNegInf, 0.0f, 0.0f, 0.0f};
+      w[sp] = live ? __builtin_amdgcn_exp2f((st.x - M) * scale_log2) : 0.0f;
+      l = __builtin_fmaf(w[sp], st.y, l);
+      const float4* __restrict__ po = part_at(sp);
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) x[sp][i] = live ? po[i] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int sp = 0; sp < kS; ++sp) combine(w[sp], x[sp]);
+  } else {
+    for (int sp = 0; sp < nsp; ++sp) {
+      if (sb[sp + 1] - sb[sp] == kListPad) continue;
+      const float4 st = pstat[((size_t)unit * nsp + sp) * kCube + row];
+      const float w = __builtin_amdgcn_exp2f((st.x - M) * scale_log2);
+      l = __builtin_fmaf(w, st.y, l);
+      const float4* __restrict__ po = part_at(sp);
+      float4 x[kVec];
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) x[i] = po[i];
+      combine(w, x);
     }
   }
   const size_t srow = (size_t)unit * kCube + row;
@@ -1060,12 +1089,23 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #undef VSA_FWD_LAUNCH
   e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  if (D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(n_units), dim3(256), 0, stream, part, pstat, sbeg,
-                       vexp, out, lse, max_prob, Nq, NH, splits, scale_log2);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(n_units), dim3(256), 0, stream, part, pstat, sbeg,
-                       vexp, out, lse, max_prob, Nq, NH, splits, scale_log2);
+#define VSA_MERGE_LAUNCH(DD, SS)                                                          \
+  hipLaunchKernelGGL((merge_kernel<DD, SS>), dim3(n_units), dim3(256), 0, stream, part, pstat, \
+                     sbeg, vexp, out, lse, max_prob, Nq, NH, splits, scale_log2)
+#define VSA_MERGE_D(DD)                           \
+  switch (splits) {                               \
+    case 2: VSA_MERGE_LAUNCH(DD, 2); break;       \
+    case 3: VSA_MERGE_LAUNCH(DD, 3); break;       \
+    case 4: VSA_MERGE_LAUNCH(DD, 4); break;       \
+    default: VSA_MERGE_LAUNCH(DD, 0); break;      \
+  }
+  if (D == 128) {
+    VSA_MERGE_D(128)
+  } else {
+    VSA_MERGE_D(64)
+  }
+#undef VSA_MERGE_D
+#undef VSA_MERGE_LAUNCH
   return hipGetLastError();
 }
 
