@@ -6,7 +6,8 @@
   with no range limit, so the output must match the oracle there too.
 * Index rows longer than the list pre-pass sorts (more than 1024 ids): the
   tile list then keeps the given id order.
-* More than 4096 query cubes: the dispatch-order pass is skipped.
+* More than 4096 query cubes: the dispatch-order pass is skipped (also with
+  key-range splits).
 
 Every unit of the first case is checked; the other two check sampled units
 against ``oracle.fwd_unit`` (plus the first and last units)."""
@@ -111,9 +112,11 @@ def test_index_rows_longer_than_the_sorted_list():
     assert_fine_ok(gpu, ref, "long rows")
 
 
-def test_more_query_cubes_than_the_dispatch_order_ranks():
+@pytest.mark.parametrize("splits", [0, 3])
+def test_more_query_cubes_than_the_dispatch_order_ranks(splits):
     """Nq = Nkv = 4100 (above the 4096 cubes the dispatch-order pass ranks),
-    topk = 4, ragged vbs: sampled units plus the first and last."""
+    topk = 4, ragged vbs: sampled units plus the first and last; also in 3
+    key-range splits (items in plain rank order)."""
     rng = np.random.default_rng(78)
     B, Nq, Nkv, NH, D, topk = 1, 4100, 4100, 1, 64, 4
     f32 = lambda *s: rng.standard_normal(s, dtype=np.float32)
@@ -123,8 +126,14 @@ def test_more_query_cubes_than_the_dispatch_order_ranks():
     vbs = rng.integers(1, 65, size=Nkv).astype(np.int32)
     idx = np.stack([rng.choice(Nkv, size=topk, replace=False) for _ in range(Nq)])
     idx = idx.reshape(B, NH, Nq, topk).astype(np.int32)
-    print(f"[Nq>4096] Nq={Nq} topk={topk}", flush=True)
-    out = _gpu_fwd(q, k, v, idx, vbs)
+    print(f"[Nq>4096] Nq={Nq} topk={topk} splits={vsa.fwd_splits(Nkv, D, topk, splits)}",
+          flush=True)
+    if splits == 0:
+        out = _gpu_fwd(q, k, v, idx, vbs)
+    else:
+        out = from_gpu_bf16(vsa.fwd_lut(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v),
+                                        torch.from_numpy(idx).cuda(), None,
+                                        torch.from_numpy(vbs).cuda(), kv_splits=splits))
     q64, k64, v64 = (oracle.decode_bf16(a) for a in (q, k, v))
     cubes = sorted(set(rng.choice(Nq, size=64, replace=False).tolist()) | {0, Nq - 1})
     gpu = {0: np.stack([out[0, c * 64:(c + 1) * 64, 0] for c in cubes])}

@@ -89,3 +89,30 @@ def test_small_workload_forced_splits_sampled_units():
         gpu[h] = np.stack([out[0, u * 64:(u + 1) * 64, h] for u in cubes])
         ref[h] = np.stack([oracle.fwd_unit(q64, k64, v64, idx, vbs, 0, h, u) for u in cubes])
     assert_fine_ok(gpu, ref, "small splits")
+
+
+@pytest.mark.parametrize("D, Nkv, topk", [(128, 1100, 100), (64, 2100, 40)])
+def test_splits_chosen_by_the_library(D, Nkv, topk):
+    """Key/value heads just above the 32 MiB the library splits at (1,100
+    cubes at D = 128, 2,100 at D = 64: 36 and 34 MB of K plus fp16 V): vsa_fwd
+    itself takes 3 splits. Every query cube (Nq = 40, two heads, ragged vbs)
+    against the oracle."""
+    rng = np.random.default_rng(65 + D)
+    B, Nq, NH = 1, 40, 2
+    assert vsa.fwd_splits(Nkv, D, topk) == 3
+    f32 = lambda *s: rng.standard_normal(s, dtype=np.float32)
+    q = synth.bf16_bits_from_f32(f32(B, Nq * 64, NH, D))
+    k = synth.bf16_bits_from_f32(f32(B, Nkv * 64, NH, D))
+    v = synth.bf16_bits_from_f32(f32(B, Nkv * 64, NH, D))
+    vbs = rng.integers(0, 65, size=Nkv).astype(np.int32)
+    idx = np.stack([np.stack([rng.choice(Nkv, size=topk, replace=False) for _ in range(Nq)])
+                    for _ in range(NH)])[None].astype(np.int32)
+    print(f"[auto splits D={D}] Nkv={Nkv} topk={topk} splits={vsa.fwd_splits(Nkv, D, topk)}",
+          flush=True)
+    out = from_gpu_bf16(vsa.fwd(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v),
+                                torch.from_numpy(idx).cuda(), torch.from_numpy(vbs).cuda()))
+    q64, k64, v64 = (oracle.decode_bf16(a) for a in (q, k, v))
+    gpu = {h: out[0, :, h].reshape(Nq, 64, D) for h in range(NH)}
+    ref = {h: np.stack([oracle.fwd_unit(q64, k64, v64, idx, vbs, 0, h, c) for c in range(Nq)])
+           for h in range(NH)}
+    assert_fine_ok(gpu, ref, f"auto splits D={D}")
