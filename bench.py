@@ -180,6 +180,10 @@ def cpu_baseline(case, seconds: float) -> dict:
     agg = float(sum(rate_each))
     whole_flops = float(np.mean([r["head_flops"] for r in res])) * case.NH
     sel_head = float(np.mean([r["select_s"] for r in res]))
+    n_cubes = -(-case.T // 4) * -(-case.H // 4) * -(-case.W // 4)
+    lo, hi = min(r["units"] for r in res), max(r["units"] for r in res)
+    units_label = (f"all {n_cubes} query cubes of each head" if lo == hi == n_cubes
+                   else f"{lo} to {hi} of the head's {n_cubes} query cubes")
     return {
         "value": agg / 1e12,
         "unit": "TFLOP/s",
@@ -187,10 +191,11 @@ def cpu_baseline(case, seconds: float) -> dict:
         "kind": "oracle",
         "sample": (f"float64 NumPy oracle: {procs} worker processes (1 BLAS thread each) on "
                    f"heads 0..{procs - 1} of the Wan workload; per worker the oracle selector "
-                   f"(top-{case.topk}) on its whole head, then the fine stage on its first "
-                   f"{min(r['units'] for r in res)}-{max(r['units'] for r in res)} query cubes "
-                   f"({seconds:.0f} s each); {sum(r['units'] for r in res)} of "
-                   f"{case.NH * 624} units in all, {wall:.1f} s wall"),
+                   f"(top-{case.topk}) on its whole head, then the fine stage on its query "
+                   f"cubes in order for at most {seconds:.0f} s ({units_label}); "
+                   f"{sum(r['units'] for r in res)} of {case.NH * n_cubes} units in all, "
+                   f"{sum(r['fwd_s'] for r in res):.1f} s of fine-stage CPU time, "
+                   f"{wall:.1f} s wall"),
         "cpu_model": model,
         "host_cores_visible": len(os.sched_getaffinity(0)),
         "blas_threads_per_process": 1,

@@ -32,6 +32,11 @@
 //   sweeps close together and move at similar rates, so they keep sharing L2
 //   lines (measured on the Wan tensors: top-78 4.23 -> 3.99 ms; a lookup
 //   table at a 0.9 mass threshold 18.5 -> 14.1 ms).
+// * Key-range splits (split-KV) for heads whose K and fp16 V exceed about
+//   32 MiB: each unit runs as S work items, item s over its selected cubes
+//   in key range s, split-major inside each head, so that the items resident
+//   on an XCD share one range of the head's keys; each item leaves a partial
+//   online-softmax state and merge_kernel combines them (fwd_splits below).
 // * K and V tiles stream through LDS, each double-buffered, loaded
 //   global -> LDS directly (buffer_load ... lds, two 1 KiB loads per M0
 //   write); wave w loads quarter w of each tile with its own descriptor. The
