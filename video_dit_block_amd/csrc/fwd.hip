@@ -882,100 +882,91 @@ __global__ __launch_bounds__(FwdShape<D>::kThreads) __attribute__((amdgpu_waves_
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the key-range splits: one workgroup per unit (b, h, query cube),
-// four threads per query row, each combining D/4 columns. With M the largest
-// reference max over the row's non-empty splits and w_s = exp2((m_s - M) c),
-// O = sum_s w_s O_s and l = sum_s w_s l_s (the online-softmax combination of
-// partial states), out = O / l * 2^e_h rounded to bf16, and the statistics
-// are the unsplit epilogue's with (M, l) and the largest row max. kS > 0:
-// exactly kS splits, every split's columns loaded before any is combined
-// (the kernel is bound by reading the partial states); kS = 0: any count.
+// Merge of the key-range splits: one workgroup of 256 threads per unit (b, h,
+// query cube). With M the largest reference max over a row's non-empty
+// splits and w_s = exp2((m_s - M) c), O = sum_s w_s O_s and l = sum_s w_s l_s
+// (the online-softmax combination of partial states), out = O / l * 2^e_h
+// rounded to bf16, and the statistics are the unsplit epilogue's with (M, l)
+// and the largest row max. The kernel is bound by reading the partial
+// states, so their reads are coalesced: an item's partial O (64 rows of D
+// fp32) is read as float4 j = t + 256 i by thread t, consecutive threads on
+// consecutive 16 bytes; thread t thus combines columns 4 (t % (D/4)) .. + 3
+// of rows t / (D/4) + (1024 / D) i. kS > 0: exactly kS splits (their loads
+// unrolled); kS = 0: any count.
 template <int D, int kS>
 __global__ __launch_bounds__(256) void merge_kernel(
     const float* __restrict__ part, const float4* __restrict__ pstat,
     const int32_t* __restrict__ sbeg, const int32_t* __restrict__ vexp,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ max_prob, int Nq,
     int NH, int splits, float scale_log2) {
-  constexpr int kCols = D / 4;
-  constexpr int kVec = kCols / 4;  // float4 per split and thread
+  constexpr int kF4 = D / 4;             // float4 per row
+  constexpr int kRowStep = 256 / kF4;    // rows apart between a thread's rows
+  constexpr int kRows = kCube / kRowStep;  // rows per thread
   const int unit = blockIdx.x;
   const int bh = unit / Nq, qc = unit - bh * Nq, h = bh % NH, b = bh / NH;
-  const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * kCols;
+  const int col4 = threadIdx.x % kF4, row0 = threadIdx.x / kF4;
   const int nsp = kS > 0 ? kS : splits;
   const int32_t* __restrict__ sb = sbeg + (size_t)unit * (nsp + 1);
-  auto part_at = [&](int sp) __attribute__((always_inline)) {
-    return reinterpret_cast<const float4*>(part + (((size_t)unit * nsp + sp) * kCube + row) * D +
-                                           c0);
-  };
-  float M = kNegInf, m_row = kNegInf;
+  const float4* __restrict__ pst = pstat + (size_t)unit * nsp * kCube;
+  const float4* __restrict__ po = reinterpret_cast<const float4*>(part) + (size_t)unit * nsp *
+                                                                             kCube * kF4;
+  float M[kRows], m_row[kRows], l[kRows];
+  float4 acc[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    M[i] = kNegInf;
+    m_row[i] = kNegInf;
+    l[i] = 0.0f;
+    acc[i] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // the row maxima, then the weighted sums
+#pragma unroll 4
   for (int sp = 0; sp < nsp; ++sp) {
     if (sb[sp + 1] - sb[sp] == kListPad) continue;  // an empty split
-    const float4 st = pstat[((size_t)unit * nsp + sp) * kCube + row];
-    M = fmaxf(M, st.x);
-    m_row = fmaxf(m_row, st.z);
-  }
-  float acc[kCols];
 #pragma unroll
-  for (int i = 0; i < kCols; ++i) acc[i] = 0.0f;
-  float l = 0.0f;
-  auto combine = [&](float w, const float4 (&x)[kVec]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      acc[4 * i] = __builtin_fmaf(w, x[i].x, acc[4 * i]);
-      acc[4 * i + 1] = __builtin_fmaf(w, x[i].y, acc[4 * i + 1]);
-      acc[4 * i + 2] = __builtin_fmaf(w, x[i].z, acc[4 * i + 2]);
-      acc[4 * i + 3] = __builtin_fmaf(w, x[i].w, acc[4 * i + 3]);
-    }
-  };
-  if constexpr (kS > 0) {
-    float4 x[kS][kVec];
-    float w[kS];
-#pragma unroll
-    for (int sp = 0; sp < kS; ++sp) {
-      const bool live = sb[sp + 1] - sb[sp] != kListPad;
-      const float4 st = live ? pstat[((size_t)unit * kS + sp) * kCube + row]
-                             : float4{kNegInf, 0.0f, 0.0f, 0.0f};
-      w[sp] = live ? __builtin_amdgcn_exp2f((st.x - M) * scale_log2) : 0.0f;
-      l = __builtin_fmaf(w[sp], st.y, l);
-      const float4* __restrict__ po = part_at(sp);
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) x[sp][i] = live ? po[i] : float4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-#pragma unroll
-    for (int sp = 0; sp < kS; ++sp) combine(w[sp], x[sp]);
-  } else {
-    for (int sp = 0; sp < nsp; ++sp) {
-      if (sb[sp + 1] - sb[sp] == kListPad) continue;
-      const float4 st = pstat[((size_t)unit * nsp + sp) * kCube + row];
-      const float w = __builtin_amdgcn_exp2f((st.x - M) * scale_log2);
-      l = __builtin_fmaf(w, st.y, l);
-      const float4* __restrict__ po = part_at(sp);
-      float4 x[kVec];
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) x[i] = po[i];
-      combine(w, x);
+    for (int i = 0; i < kRows; ++i) {
+      const float4 st = pst[sp * kCube + row0 + kRowStep * i];
+      M[i] = fmaxf(M[i], st.x);
+      m_row[i] = fmaxf(m_row[i], st.z);
     }
   }
-  const size_t srow = (size_t)unit * kCube + row;
-  if ((threadIdx.x & 3) == 0) {
-    if (lse != nullptr)
-      lse[srow] = l > 0.0f ? (M * scale_log2 - kPShift + __log2f(l)) * 0.69314718055994531f
-                           : kNegInf;
-    if (max_prob != nullptr)
-      max_prob[srow] =
-          l > 0.0f ? __builtin_amdgcn_exp2f((m_row - M) * scale_log2 + kPShift) / l : 0.0f;
+#pragma unroll 4
+  for (int sp = 0; sp < nsp; ++sp) {
+    if (sb[sp + 1] - sb[sp] == kListPad) continue;
+    float4 x[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) x[i] = po[(size_t)sp * kCube * kF4 + threadIdx.x + 256 * i];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const float4 st = pst[sp * kCube + row0 + kRowStep * i];
+      const float w = __builtin_amdgcn_exp2f((st.x - M[i]) * scale_log2);
+      l[i] = __builtin_fmaf(w, st.y, l[i]);
+      acc[i].x = __builtin_fmaf(w, x[i].x, acc[i].x);
+      acc[i].y = __builtin_fmaf(w, x[i].y, acc[i].y);
+      acc[i].z = __builtin_fmaf(w, x[i].z, acc[i].z);
+      acc[i].w = __builtin_fmaf(w, x[i].w, acc[i].w);
+    }
   }
   const int ve = vexp == nullptr ? 0 : vexp[bh];
-  const float inv_l = l > 0.0f ? ldexpf(1.0f / l, ve) : 0.0f;
-  uint16_t* __restrict__ orow =
-      out + (((size_t)b * Nq + qc) * kCube + row) * (size_t)NH * D + (size_t)h * D + c0;
 #pragma unroll
-  for (int i = 0; i < kCols / 8; ++i) {
-    const u32x4 w4 = {pack_bf16x2(acc[8 * i] * inv_l, acc[8 * i + 1] * inv_l),
-                      pack_bf16x2(acc[8 * i + 2] * inv_l, acc[8 * i + 3] * inv_l),
-                      pack_bf16x2(acc[8 * i + 4] * inv_l, acc[8 * i + 5] * inv_l),
-                      pack_bf16x2(acc[8 * i + 6] * inv_l, acc[8 * i + 7] * inv_l)};
-    *reinterpret_cast<u32x4*>(orow + 8 * i) = w4;
+  for (int i = 0; i < kRows; ++i) {
+    const int row = row0 + kRowStep * i;
+    const size_t srow = (size_t)unit * kCube + row;
+    if (col4 == 0) {
+      if (lse != nullptr)
+        lse[srow] = l[i] > 0.0f
+                        ? (M[i] * scale_log2 - kPShift + __log2f(l[i])) * 0.69314718055994531f
+                        : kNegInf;
+      if (max_prob != nullptr)
+        max_prob[srow] = l[i] > 0.0f ? __builtin_amdgcn_exp2f((m_row[i] - M[i]) * scale_log2 +
+                                                              kPShift) / l[i]
+                                     : 0.0f;
+    }
+    const float inv_l = l[i] > 0.0f ? ldexpf(1.0f / l[i], ve) : 0.0f;
+    uint16_t* __restrict__ orow = out + (((size_t)b * Nq + qc) * kCube + row) * (size_t)NH * D +
+                                  (size_t)h * D + 4 * col4;
+    *reinterpret_cast<u32x2*>(orow) = u32x2{pack_bf16x2(acc[i].x * inv_l, acc[i].y * inv_l),
+                                            pack_bf16x2(acc[i].z * inv_l, acc[i].w * inv_l)};
   }
 }
 
