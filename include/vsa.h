@@ -234,8 +234,8 @@ int32_t vsa_fwd_splits(int32_t Nkv, int32_t D, int32_t topk, int32_t kv_splits);
  * query cube) (B * NH * Nq of them), the list of the 32-row tiles that hold
  * real tokens of its selected cubes ((2 * topk + 4 + (S > 1 ? S : 0))
  * entries of two uint32), the first tile of each split and the tile count
- * (S + 1 int32), its dispatch rank (one int32) and the rank's sort key (two
- * int32); then the largest |v| of every (v pre-pass workgroup, head)
+ * (S + 1 int32), the cube at each dispatch position and each cube's dispatch
+ * position (one int32 each) and the positions' sort key (two int32); then the largest |v| of every (v pre-pass workgroup, head)
  * (B * Nkv * 8 * NH float32), the per-(b, h) exponent of the fp16 copy
  * (B * NH int32) and, with S > 1 splits (vsa_fwd_splits), the partial
  * results (B * NH * Nq * S * 64 * (D + 4) float32), each part 256-byte

@@ -105,11 +105,12 @@ def test_fwd_validation():
     # fp16 v (8 cubes x 64 rows x 2 heads x 64 x 2 bytes), then the tile
     # lists of the 16 (head, query cube) units ((2 * 3 + 4) tiles x 8 bytes
     # each = 1280 bytes), then their first and end tiles (16 x 2 int32 -> 256
-    # after 256-byte rounding), their dispatch ranks (16 int32 -> 256) and the ranks' sort
-    # keys (16 x 2 int32 -> 256), then the largest |v| of every (v pre-pass
+    # after 256-byte rounding), the cube at each dispatch position and each
+    # cube's position (16 int32 -> 256 each) and the positions' sort keys
+    # (16 x 2 int32 -> 256), then the largest |v| of every (v pre-pass
     # workgroup, head) (8 cubes x 8 workgroups x 2 heads float32 = 512) and
     # the per-head exponent of the fp16 copy (2 int32 -> 256)
-    need = 8 * 64 * 2 * 64 * 2 + 1280 + 256 + 256 + 256 + 512 + 256
+    need = 8 * 64 * 2 * 64 * 2 + 1280 + 256 + 256 + 256 + 256 + 512 + 256
     assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 3) == need
     assert lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 0) == 0
     assert call(ws=None) == _lib.VSA_ERR_WORKSPACE
@@ -139,11 +140,11 @@ def test_fwd_splits_choice_and_workspace():
     assert lib.vsa_fwd_splits(8, 64, 9, 0) == 0
     # 3 splits of 16 units: lists of 2 * 3 + 4 + 3 * 5 tiles (a zero quarter
     # and 4 zero tiles per split) x 8 bytes = 3200 -> 3328, first tiles
-    # (16 x 4 int32 = 256), ranks and keys (256 + 256), |v| maxima (512),
-    # exponents (256), partial O (16 x 3 x 64 x 64 float32) and partial row
-    # states (16 x 3 x 64 float4)
-    need = 8 * 64 * 2 * 64 * 2 + 3328 + 256 + 256 + 256 + 512 + 256 + 16 * 3 * 64 * 64 * 4 + \
-        16 * 3 * 64 * 16
+    # (16 x 4 int32 = 256), order, positions and keys (256 + 256 + 256), |v|
+    # maxima (512), exponents (256), partial O (16 x 3 x 64 x 64 float32) and
+    # partial row states (16 x 3 x 64 float4)
+    need = 8 * 64 * 2 * 64 * 2 + 3328 + 256 + 256 + 256 + 256 + 512 + 256 + \
+        16 * 3 * 64 * 64 * 4 + 16 * 3 * 64 * 16
     assert lib.vsa_fwd_workspace_bytes_ex(1, 8, 8, 2, 64, 3, 3) == need
     assert lib.vsa_fwd_workspace_bytes_ex(1, 8, 8, 2, 64, 3, 0) == \
         lib.vsa_fwd_workspace_bytes(1, 8, 8, 2, 64, 3)

@@ -371,14 +371,32 @@ __global__ __launch_bounds__(kCvtThreads) void vfix_kernel(
 // sbeg[unit][s] is the first tile of split s (of the list: s = 0) and
 // sbeg[unit][splits] the end of the list, so split s has
 // sbeg[s + 1] - sbeg[s] - kListPad tiles.
+//
+// Rotated sweeps (rank_of != NULL; unsplit sorted rows): the units resident
+// on an XCD at one time are about kSweepWindow consecutive dispatch
+// positions. Once their run times drift apart, units that started at
+// different times sweep different parts of the key range, and their tiles
+// stop sharing L2 lines. So a unit's ascending sweep starts at key id
+// (p mod W) * Nkv / W, where p is its dispatch position on its XCD and
+// W = kSweepWindow, and wraps around to the lower ids. A unit that starts
+// when the one W positions earlier ends then meets the resident units at
+// the same key position. On the Wan tensors this measured 3.85-3.91 ->
+// 3.69 ms at top-78, 16.1-16.5 -> 14.3-14.5 ms at top-312 and 9.4 -> 8.6 ms
+// at top-187. A row that selects every key cube (dense) keeps the plain
+// sweep: such units never drift, and rotating them cost 5%. The rotation
+// depends only on the row's ids, its count and the dispatch position, so a
+// lookup-table row equal to a top-k row gives the same list.
 constexpr int kListSortCap = 1024;
 constexpr int kListPad = 4;
 constexpr int kQuarter = 16;  // rows per quarter
+// fine-kernel units resident per XCD on MI355X: 32 CUs x 4 workgroups
+constexpr int kSweepWindow = 128;
 
 __global__ __launch_bounds__(64) void tiles_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ valid,
     const int32_t* __restrict__ vbs, uint32_t* __restrict__ list, int32_t* __restrict__ sbeg,
-    int Nkv, int row_len, int stride, uint32_t rs2, int splits) {
+    int Nkv, int row_len, int stride, uint32_t rs2, int splits,
+    const int32_t* __restrict__ rank_of, int Nq, int n_units) {
   __shared__ int32_t keys[kListSortCap];
   __shared__ int32_t qcount[kMaxSplits];  // quarters of split s
   __shared__ int32_t qpad[kMaxSplits];    // zero quarters placed before split s
@@ -441,13 +459,28 @@ __global__ __launch_bounds__(64) void tiles_kernel(
       if (lane < 2 * kListPad + 1 && (lane > 0 || (qcount[sp] & 1)))
         out[qend[sp] - 1 + lane] = 0u;
   }
+  // rotated sweep: the list starts at sorted position k0, the first id at
+  // or above the unit's start key id
+  int k0 = 0;
+  if (rank_of != nullptr && sorted && splits == 1 && topk > 0 && topk < Nkv) {
+    const int lin = unit - unit % Nq + min(max(rank_of[unit], 0), Nq - 1);
+    const int q8 = n_units / kNumXcd, r8 = n_units % kNumXcd;
+    int x = 0;  // the XCD that runs dispatch position lin (xcd_remap's ranges)
+    while (x < kNumXcd - 1 && lin >= (x + 1) * q8 + min(x + 1, r8)) ++x;
+    const int p = lin - (x * q8 + min(x, r8));
+    const int start = (int)(((int64_t)(p % kSweepWindow) * Nkv) / kSweepWindow);
+    int below_start = 0;
+    for (int i = lane; i < topk; i += 64) below_start += keys[i] < start;
+    for (int o = 32; o > 0; o >>= 1) below_start += __shfl_xor(below_start, o, 64);
+    k0 = below_start == topk ? 0 : below_start;
+  }
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   int base = 0;  // quarters written so far, without the zero quarters
   for (int c0 = 0; c0 < topk; c0 += 64) {
     const int i = c0 + lane;
     int id = 0, nv = 0;
     if (i < topk) {
-      id = sorted ? keys[i] : id_at(i);
+      id = sorted ? keys[k0 == 0 ? i : (i + k0) % topk] : id_at(i);
       nv = min(max(vbs[id], 0), kCube);
     }
     const int nq = (nv + kQuarter - 1) / kQuarter;  // 0..4
@@ -507,7 +540,8 @@ __global__ __launch_bounds__(kOrderThreads) void order_key_kernel(
 }
 
 __global__ __launch_bounds__(kOrderThreads) void order_rank_kernel(
-    const uint64_t* __restrict__ keys, int32_t* __restrict__ order, int Nq) {
+    const uint64_t* __restrict__ keys, int32_t* __restrict__ order, int32_t* __restrict__ rank_of,
+    int Nq) {
   extern __shared__ uint64_t key[];
   const size_t base = (size_t)blockIdx.x * Nq;
   for (int i = threadIdx.x; i < Nq; i += kOrderThreads) key[i] = keys[base + i];
@@ -519,6 +553,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_rank_kernel(
 #pragma unroll 8
   for (int j = 0; j < Nq; ++j) rank += key[j] < ki;
   order[base + rank] = i;
+  rank_of[base + i] = rank;
 }
 
 // ---------------------------------------------------------------------------
@@ -1006,7 +1041,8 @@ FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk, int 
   w.list_off = up((size_t)B * Nkv * kCube * NH * D * 2);
   w.sbeg_off = w.list_off + up(units * w.list_stride * 8);
   w.order_off = w.sbeg_off + up(units * (w.splits + 1) * 4);
-  w.key_off = w.order_off + up(units * 4);
+  w.rank_off = w.order_off + up(units * 4);
+  w.key_off = w.rank_off + up(units * 4);
   w.vmax_off = w.key_off + up(units * 8);
   w.vexp_off = w.vmax_off + up((size_t)B * Nkv * kCvtSplit * NH * 4);
   w.part_off = w.vexp_off + up((size_t)B * NH * 4);
@@ -1032,6 +1068,7 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   uint32_t* vmax = reinterpret_cast<uint32_t*>(ws + w.vmax_off);
   int32_t* vexp = reinterpret_cast<int32_t*>(ws + w.vexp_off);
   int32_t* order = nullptr;
+  int32_t* rank_of = nullptr;
   const int n_units = B * NH * Nq;
   hipLaunchKernelGGL(v_to_fp16_kernel, dim3(Nkv * kCvtSplit, B), dim3(kCvtThreads), 0, stream,
                      reinterpret_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(v16), vbs, vmax,
@@ -1059,13 +1096,16 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        (int64_t)n_units);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    rank_of = reinterpret_cast<int32_t*>(ws + w.rank_off);
     hipLaunchKernelGGL(order_rank_kernel, dim3(B * NH, (Nq + kOrderThreads - 1) / kOrderThreads),
-                       dim3(kOrderThreads), (size_t)Nq * sizeof(uint64_t), stream, keys, order, Nq);
+                       dim3(kOrderThreads), (size_t)Nq * sizeof(uint64_t), stream, keys, order,
+                       rank_of, Nq);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(tiles_kernel, dim3(n_units), dim3(64), 0, stream, topk_idx, valid, vbs,
-                     list, sbeg, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u, splits);
+                     list, sbeg, Nkv, topk, w.list_stride, (uint32_t)NH * D * 2u, splits,
+                     rank_of, Nq, n_units);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);

@@ -75,13 +75,14 @@ int fwd_splits(int Nkv, int D, int topk, int forced);
 // Workspace carve-up of vsa_fwd: an fp16 copy of v in the tiled layout, the
 // tile lists of the units ([B*NH*Nq][list_stride] pairs of uint32 quarters),
 // the first tile of every split of a unit ([B*NH*Nq][splits + 1]), the
-// dispatch order and its sort keys, the per-(workgroup, head) maxima of |v|,
-// the per-(b, h) exponent of v's fp16 copy, and with splits the partial
-// results: O as fp32 [B*NH*Nq*splits][64][D] and (m, l, row max, 0) as
-// float4 [B*NH*Nq*splits][64].
+// dispatch order, each unit's dispatch rank and the order's sort keys, the
+// per-(workgroup, head) maxima of |v|, the per-(b, h) exponent of v's fp16
+// copy, and with splits the partial results: O as fp32
+// [B*NH*Nq*splits][64][D] and (m, l, row max, 0) as float4
+// [B*NH*Nq*splits][64].
 struct FwdWorkspace {
-  size_t v16_off, list_off, sbeg_off, order_off, key_off, vmax_off, vexp_off, part_off,
-      pstat_off, total;
+  size_t v16_off, list_off, sbeg_off, order_off, rank_off, key_off, vmax_off, vexp_off,
+      part_off, pstat_off, total;
   int list_stride, splits;
 };
 FwdWorkspace fwd_workspace(int B, int Nq, int Nkv, int NH, int D, int topk, int forced = 0);
