@@ -385,7 +385,9 @@ __global__ __launch_bounds__(kCvtThreads) void vfix_kernel(
 // at top-187. A row that selects every key cube (dense) keeps the plain
 // sweep: such units never drift, and rotating them cost 5%. The rotation
 // depends only on the row's ids, its count and the dispatch position, so a
-// lookup-table row equal to a top-k row gives the same list.
+// lookup-table row equal to a top-k row gives the same list. With key-range
+// splits each split's sweep rotates the same way inside the split's range,
+// by the item's own dispatch position.
 constexpr int kListSortCap = 1024;
 constexpr int kListPad = 4;
 constexpr int kQuarter = 16;  // rows per quarter
@@ -401,6 +403,9 @@ __global__ __launch_bounds__(64) void tiles_kernel(
   __shared__ int32_t qcount[kMaxSplits];  // quarters of split s
   __shared__ int32_t qpad[kMaxSplits];    // zero quarters placed before split s
   __shared__ int32_t qend[kMaxSplits];    // first quarter after split s's tiles
+  __shared__ int32_t qbeg[kMaxSplits];    // first quarter of split s
+  __shared__ int32_t qstart[kMaxSplits];  // key id split s's rotated sweep starts at
+  __shared__ int32_t qbelow[kMaxSplits];  // quarters of split s below that id
   const int unit = blockIdx.x, lane = threadIdx.x;
   const int32_t* __restrict__ sel = topk_idx + (size_t)unit * row_len;
   // the row's first `topk` ids are used: all of them, or valid[unit] (clamped)
@@ -432,13 +437,38 @@ __global__ __launch_bounds__(64) void tiles_kernel(
   auto split_of = [&](int id) __attribute__((always_inline)) -> int {
     return (int)(((int64_t)id * splits) / Nkv);
   };
+  // dispatch position on its XCD of work item (unit, split sp): the items
+  // run split-major inside each (b, h), in rank order, and xcd_remap hands
+  // each XCD a contiguous range of them
+  const bool rotate = rank_of != nullptr && sorted && topk > 0 && topk < Nkv;
+  auto xcd_position = [&](int sp) __attribute__((always_inline)) -> int {
+    const int n_items = n_units * splits;
+    const int bh = unit / Nq;
+    const int lin = (bh * splits + sp) * Nq + min(max(rank_of[unit], 0), Nq - 1);
+    const int q8 = n_items / kNumXcd, r8 = n_items % kNumXcd;
+    int x = 0;
+    while (x < kNumXcd - 1 && lin >= (x + 1) * q8 + min(x + 1, r8)) ++x;
+    return lin - (x * q8 + min(x, r8));
+  };
   if (splits > 1) {  // the host allows splits only for sorted rows
-    if (lane < kMaxSplits) qcount[lane] = 0;
+    if (lane < kMaxSplits) {
+      qcount[lane] = 0;
+      qbelow[lane] = 0;
+    }
+    if (lane < splits) {  // split lane: ids [lo, hi); its sweep starts inside
+      const int lo = (int)(((int64_t)lane * Nkv + splits - 1) / splits);
+      const int hi = (int)(((int64_t)(lane + 1) * Nkv + splits - 1) / splits);
+      qstart[lane] = rotate ? lo + (int)(((int64_t)(xcd_position(lane) % kSweepWindow) *
+                                          (hi - lo)) / kSweepWindow)
+                            : lo;
+    }
     __syncthreads();
     for (int i = lane; i < topk; i += 64) {
       const int id = keys[i];
       const int nv = min(max(vbs[id], 0), kCube);
-      atomicAdd(&qcount[split_of(id)], (nv + kQuarter - 1) / kQuarter);
+      const int sp = split_of(id), nq = (nv + kQuarter - 1) / kQuarter;
+      atomicAdd(&qcount[sp], nq);
+      if (id < qstart[sp]) atomicAdd(&qbelow[sp], nq);
     }
     __syncthreads();
     if (lane == 0) {
@@ -446,6 +476,7 @@ __global__ __launch_bounds__(64) void tiles_kernel(
       for (int sp = 0; sp < splits; ++sp) {
         const int qn = qcount[sp];
         qpad[sp] = pad;
+        qbeg[sp] = start;
         sb[sp] = start / 2;
         qend[sp] = start + qn + (qn & 1);
         pad += (qn & 1) + 2 * kListPad;
@@ -462,13 +493,8 @@ __global__ __launch_bounds__(64) void tiles_kernel(
   // rotated sweep: the list starts at sorted position k0, the first id at
   // or above the unit's start key id
   int k0 = 0;
-  if (rank_of != nullptr && sorted && splits == 1 && topk > 0 && topk < Nkv) {
-    const int lin = unit - unit % Nq + min(max(rank_of[unit], 0), Nq - 1);
-    const int q8 = n_units / kNumXcd, r8 = n_units % kNumXcd;
-    int x = 0;  // the XCD that runs dispatch position lin (xcd_remap's ranges)
-    while (x < kNumXcd - 1 && lin >= (x + 1) * q8 + min(x + 1, r8)) ++x;
-    const int p = lin - (x * q8 + min(x, r8));
-    const int start = (int)(((int64_t)(p % kSweepWindow) * Nkv) / kSweepWindow);
+  if (rotate && splits == 1) {
+    const int start = (int)(((int64_t)(xcd_position(0) % kSweepWindow) * Nkv) / kSweepWindow);
     int below_start = 0;
     for (int i = lane; i < topk; i += 64) below_start += keys[i] < start;
     for (int o = 32; o > 0; o >>= 1) below_start += __shfl_xor(below_start, o, 64);
@@ -484,13 +510,18 @@ __global__ __launch_bounds__(64) void tiles_kernel(
       nv = min(max(vbs[id], 0), kCube);
     }
     const int nq = (nv + kQuarter - 1) / kQuarter;  // 0..4
-    int pos = base + (splits > 1 && i < topk ? qpad[split_of(id)] : 0), tot = 0;
+    const int sp = splits > 1 && i < topk ? split_of(id) : 0;
+    int pos = base + (splits > 1 && i < topk ? qpad[sp] : 0), tot = 0;
 #pragma unroll
     for (int k = 1; k <= kCube / kQuarter; ++k) {
       const uint64_t bk = __builtin_amdgcn_ballot_w64(nq >= k);
       pos += __builtin_popcountll(bk & below);
       tot += __builtin_popcountll(bk);
     }
+    // split sp's quarters in rotated order: the cube's offset inside the
+    // split, less the quarters below the split's start id, modulo the split
+    if (splits > 1 && nq > 0 && qbelow[sp] > 0)
+      pos = qbeg[sp] + (pos - qbeg[sp] - qbelow[sp] + qcount[sp]) % qcount[sp];
     const uint32_t off0 = (uint32_t)id * (uint32_t)kCube * rs2;
     for (int k = 0; k < nq; ++k)
       out[pos + k] = (off0 + (uint32_t)(kQuarter * k) * rs2) | (uint32_t)min(nv - kQuarter * k, kQuarter);
