@@ -223,7 +223,7 @@ int32_t vsa_select_cdf(const vsa_bf16_t* q_tiled, const vsa_bf16_t* k_tiled,
  * pass combines their partial softmax states (the result is that of the
  * unsplit stage up to fp32 rounding order). kv_splits: 0 chooses (S > 1 only
  * once one head's K plus its fp16 V copy, Nkv * 64 * D * 4 bytes, exceeds
- * 32 MiB: about 16 MiB of them per split, at least 8 selected cubes per split
+ * 32 MiB: about 32 MiB of them per split, at least 8 selected cubes per split
  * on average, at most 16), 1 turns splitting off, 2..16 asks for that many.
  * Rows of more than 1024 ids are never split. Returns 0 for invalid
  * arguments (kv_splits outside [0, 16], topk outside [1, Nkv]). Host-only. */

@@ -122,14 +122,15 @@ def test_fwd_validation():
 
 def test_fwd_splits_choice_and_workspace():
     """The key-range split count: none at the Wan shape (a head's K and fp16 V
-    copy, 624 x 64 x 128 x 4 bytes = 20 MB, stay under 32 MiB), 4 at the 720p
-    shape (1920 cubes: 63 MB in splits of about 16 MiB), at most topk / 8,
-    never for rows longer than 1024 ids; forced counts are taken as given.
-    With splits the workspace adds the partial results."""
+    copy, 624 x 64 x 128 x 4 bytes = 20 MB, stay under 32 MiB), 2 at the 720p
+    shape (1920 cubes: 63 MB in splits of about 32 MiB), 4 at 4,096 cubes, at
+    most topk / 8, never for rows longer than 1024 ids; forced counts are
+    taken as given. With splits the workspace adds the partial results."""
     lib = _lib.load()
     assert lib.vsa_fwd_splits(624, 128, 78, 0) == 1
-    assert lib.vsa_fwd_splits(1920, 128, 192, 0) == 4
-    assert lib.vsa_fwd_splits(1920, 128, 24, 0) == 3
+    assert lib.vsa_fwd_splits(1920, 128, 192, 0) == 2
+    assert lib.vsa_fwd_splits(4096, 128, 192, 0) == 4
+    assert lib.vsa_fwd_splits(4096, 128, 24, 0) == 3
     assert lib.vsa_fwd_splits(1920, 128, 8, 0) == 1
     assert lib.vsa_fwd_splits(1920, 128, 1100, 0) == 1
     assert lib.vsa_fwd_splits(1920, 128, 1100, 4) == 1

@@ -8,7 +8,7 @@ Forced split counts on small ragged inputs, every row against the oracle
 under the fine stage's acceptance rule, with the per-row statistics under the
 bounds of test_gpu_6_lut: splits that no selected cube falls in, more splits
 than key cubes, rows with no keys, per-row counts, B = 2, both D. A split
-count of 1 is the unsplit stage bit for bit. The 720p workload takes 4 splits
+count of 1 is the unsplit stage bit for bit. The 720p workload takes 2 splits
 by itself (test_gpu_5_hy720 runs it)."""
 import numpy as np
 import pytest
@@ -95,11 +95,11 @@ def test_small_workload_forced_splits_sampled_units():
 def test_splits_chosen_by_the_library(D, Nkv, topk):
     """Key/value heads just above the 32 MiB the library splits at (1,100
     cubes at D = 128, 2,100 at D = 64: 36 and 34 MB of K plus fp16 V): vsa_fwd
-    itself takes 3 splits. Every query cube (Nq = 40, two heads, ragged vbs)
+    itself takes 2 splits. Every query cube (Nq = 40, two heads, ragged vbs)
     against the oracle."""
     rng = np.random.default_rng(65 + D)
     B, Nq, NH = 1, 40, 2
-    assert vsa.fwd_splits(Nkv, D, topk) == 3
+    assert vsa.fwd_splits(Nkv, D, topk) == 2
     f32 = lambda *s: rng.standard_normal(s, dtype=np.float32)
     q = synth.bf16_bits_from_f32(f32(B, Nq * 64, NH, D))
     k = synth.bf16_bits_from_f32(f32(B, Nkv * 64, NH, D))

@@ -1042,19 +1042,22 @@ __global__ __launch_bounds__(256) void merge_kernel(
 // run side by side on an XCD sweep that head's keys; once one head's K and
 // fp16 V exceed about 32 MiB (a few times the XCD's 4 MiB L2) their tiles are
 // evicted before the other units reach them, and the kernel fetches many
-// times its algorithmic bytes from beyond L2 (measured at the 720p shape:
-// 65x, 29% L2 hits, 7.3 TB/s). Split into S key ranges of about 16 MiB, run
-// split-major inside each head, the resident units share one range; each
-// item leaves a partial state that merge_kernel combines. forced: 0 chooses,
-// 1 turns splitting off, 2..kMaxSplits forces S. Rows longer than the sorted
-// list pre-pass allows (kListSortCap ids) are never split.
+// times its algorithmic bytes from beyond L2 (measured at the 720p shape
+// before rotated sweeps: 65x, 29% L2 hits, 7.3 TB/s). Split into S key
+// ranges of about 32 MiB, run split-major inside each head, the resident
+// units share one range; each item leaves a partial state that merge_kernel
+// combines. Measured at the 720p shape (63 MB per head) with rotated sweeps:
+// S = 1 21.6 ms, 2 20.9, 3 21.2, 4 21.7, 8 24.1 (every split adds a partial
+// state per unit). forced: 0 chooses, 1 turns splitting off, 2..kMaxSplits
+// forces S. Rows longer than the sorted list pre-pass allows (kListSortCap
+// ids) are never split.
 int fwd_splits(int Nkv, int D, int topk, int forced) {
   if (topk > kListSortCap) return 1;
   if (forced > 0) return forced < kMaxSplits ? forced : kMaxSplits;
   const double kv_head = (double)Nkv * kCube * D * 4.0;  // K bf16 + V fp16
   const double mib = 1024.0 * 1024.0;
   if (kv_head <= 32.0 * mib) return 1;
-  int sp = (int)ceil(kv_head / (16.0 * mib));
+  int sp = (int)ceil(kv_head / (32.0 * mib));
   sp = sp < topk / 8 ? sp : topk / 8;  // at least 8 selected cubes per item on average
   return sp < 2 ? 1 : (sp < kMaxSplits ? sp : kMaxSplits);
 }
