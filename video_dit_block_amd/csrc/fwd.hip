@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kCvtThreads) void vfix_kernel(
 // sbeg[unit][splits] the end of the list, so split s has
 // sbeg[s + 1] - sbeg[s] - kListPad tiles.
 //
-// Rotated sweeps (rank_of != NULL; unsplit sorted rows): the units resident
+// Rotated sweeps (rank_of != NULL; sorted rows): the units resident
 // on an XCD at one time are about kSweepWindow consecutive dispatch
 // positions. Once their run times drift apart, units that started at
 // different times sweep different parts of the key range, and their tiles
