@@ -215,8 +215,9 @@ using IC = std::integral_constant<int, N>;
 // (clamped to [-90, 113]), which puts its largest magnitude in [2^14, 2^15);
 // multiplying by a power of two is exact, and the fine kernel multiplies the
 // head's output rows by 2^e_h. Three launches:
-//   v_to_fp16_kernel: real rows converted with e = 0, padding rows zeroed, and
-//     the largest |v| of every (workgroup, head) written to vmax;
+//   v_to_fp16_kernel: real rows converted with e = 0 (padding rows are never
+//                     read, so not written), and the largest |v| of every
+//                     (workgroup, head) written to vmax;
 //   vscale_kernel:    per (b, h), e_h from the largest of those maxima;
 //   vfix_kernel:      the rows of heads with e_h != 0 converted again, scaled.
 // Only the first is HBM-bound (one read and one write of v); the other two
@@ -281,10 +282,10 @@ __global__ __launch_bounds__(kCvtThreads) void v_to_fp16_kernel(
 #pragma unroll
     for (int i = 0; i < kCvtColBlk; ++i) {
       const int col = c0 + 64 * i + lane;
-      if (col < cpr) {
-        dst0[col] = bf16x8_to_fp16x8(w0[i]);  // zeros for padding rows
-        dst1[col] = bf16x8_to_fp16x8(w1[i]);
-      }
+      // real rows only: the fine kernel's loads never reach padding rows
+      // (a load's buffer range ends at its quarter's real rows)
+      if (col < cpr && u0 < nv) dst0[col] = bf16x8_to_fp16x8(w0[i]);
+      if (col < cpr && u1 < nv) dst1[col] = bf16x8_to_fp16x8(w1[i]);
       // largest |v| of the head's chunks in these two rows: reduce over the
       // cph lanes of each head (heads start at multiples of cph lanes)
       uint32_t m = max(bf16x8_absmax_bits(w0[i]), bf16x8_absmax_bits(w1[i]));
@@ -325,13 +326,18 @@ __global__ __launch_bounds__(256) void vscale_kernel(const uint32_t* __restrict_
 }
 
 // grid (Nkv * kCvtSplit, B): the real rows of every head with e_h != 0,
-// converted again with the scale 2^-e_h (padding rows are zero already).
+// converted again with the scale 2^-e_h.
 __global__ __launch_bounds__(kCvtThreads) void vfix_kernel(
     const uint32_t* __restrict__ v, uint32_t* __restrict__ v16, const int32_t* __restrict__ vbs,
     const int32_t* __restrict__ vexp, int Nkv, int NH, int D) {
   const int c = blockIdx.x / kCvtSplit, part = blockIdx.x % kCvtSplit, b = blockIdx.y;
-  const int nv = min(max(vbs[c], 0), kCube);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  // the common case, no head of the batch scaled: one load per lane, leave
+  bool any = false;
+  for (int h0 = 0; h0 < NH; h0 += 64)
+    any |= __builtin_amdgcn_ballot_w64(h0 + lane < NH && vexp[(size_t)b * NH + h0 + lane] != 0) != 0;
+  if (!any) return;
+  const int nv = min(max(vbs[c], 0), kCube);
   const int wpr = NH * D / 2;  // 32-bit words (bf16 pairs) per row
   for (int h = 0; h < NH; ++h) {
     const int e = vexp[(size_t)b * NH + h];
