@@ -15,13 +15,13 @@ topk in {624, 312, 187, 78, 31}. Further legs on the same tensors: the
 lookup-table path (cumulative-mass selector + vsa_fwd_lut with its row
 statistics), the two-stage path (coarse output, gated combine), the fine
 kernel in Hilbert cube order, and the block mask -> LUT compaction; then the
-whole path on the 720p HunyuanVideo-like workload. Context measured in the
-same run: the engine clock during the timed vsa_fwd loop (a shader-cycle
-meter on a second stream, in a repeat of the loop), and two bf16 ceilings of
-this part, a bounded MFMA-only loop on random operands and a large hipBLASLt
-GEMM. The CPU oracle is timed on a bounded
-sample of the same workload, in one process per core, as a reported
-baseline.
+whole path on the 720p HunyuanVideo-like workload. The Wan step is also
+timed back to back, eagerly and replayed as one captured HIP graph. Context
+measured in the same run: the engine clock during the timed vsa_fwd loop (a
+shader-cycle meter on a second stream, in a repeat of the loop), and two bf16
+ceilings of this part, a bounded MFMA-only loop on random operands and a
+large hipBLASLt GEMM. The CPU oracle is timed on a bounded sample of the same
+workload, in one process per core, as a reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-hy720] [--no-cpu]
        python bench.py --fwd-only [--fwd-workload wan|hy720] ...   (profiler mode: vsa_fwd
@@ -474,6 +474,34 @@ def main():
     parts /= args.steps
     step_ms = float(parts.sum())
 
+    # the step back to back, eagerly and as one captured HIP graph (no entry
+    # point allocates, sets memory or synchronises, so a step captures whole)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(args.steps):
+        step(False)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(False)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / args.steps
+    del graph
+
     # the fine forward alone, back to back (kernel-only, warmed), with the
     # engine clock sampled while it runs
     e0, e1 = ev(), ev()
@@ -705,6 +733,7 @@ def main():
                               "fwd": round(parts[2], 4), "untile": round(parts[3], 4)},
         "tile_qkv_gbs": round(tile_bytes / (parts[0] * 1e-3) / 1e9, 1),
         "wall_ms_per_step": round(wall, 3),
+        "step_back_to_back_ms": {"eager": round(eager_ms, 4), "hip_graph": round(graph_ms, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": profiled_traffic()},
