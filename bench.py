@@ -249,10 +249,11 @@ class ClockMeter:
 
 
 def bf16_ceilings(torch, dev, clock) -> dict:
-    """Two measured bf16 rates of this part, context for the fine kernel's:
-    a bounded MFMA-only loop on random operands (libvsa_probe.so, about 0.5 s)
-    and torch.matmul bf16 at 16384^3 (hipBLASLt), each timed with events after
-    a warm-up long enough for the clock to settle."""
+    """Measured bf16 rates of this part, context for the fine kernel's: a
+    bounded MFMA-only loop on random operands (libvsa_probe.so, about 0.5 s),
+    the same loop carrying the fine kernel's vector work at its occupancy, and
+    torch.matmul bf16 at 16384^3 (hipBLASLt), each timed with events after a
+    warm-up long enough for the clock to settle."""
     import ctypes
 
     out = {}
@@ -286,6 +287,33 @@ def bf16_ceilings(torch, dev, clock) -> dict:
     out["mfma_loop_tflops"] = round(lib.vsa_probe_mfma_flop(blocks, iters) / ms / 1e9, 1)
     out["mfma_loop"] = ("v_mfma_f32_32x32x16_bf16 on random bf16 operands read from LDS, "
                         "4 waves per workgroup, 4 workgroups per CU, 1024 workgroups")
+    # the same MFMAs with the fine kernel's vector work and occupancy
+    lib.vsa_probe_mfma_mix.restype = ctypes.c_int32
+    lib.vsa_probe_mfma_mix.argtypes = lib.vsa_probe_mfma.argtypes
+    lib.vsa_probe_mfma_mix_flop.restype = ctypes.c_double
+    lib.vsa_probe_mfma_mix_flop.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    mblocks = 2048
+    mres = torch.empty(mblocks * 128, dtype=torch.float32, device=dev)
+    mrun = lambda: lib.vsa_probe_mfma_mix(src.data_ptr(), slots, mblocks, iters, mres.data_ptr(),
+                                          stream)
+    for _ in range(8):
+        assert mrun() == 0
+    e0.record()
+    for _ in range(20):
+        mrun()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 20
+    clock.start(span_ms=100.0)
+    for _ in range(20):
+        mrun()
+    out["mfma_vector_loop_clock"] = clock.stop()
+    out["mfma_vector_loop_tflops"] = round(lib.vsa_probe_mfma_mix_flop(mblocks, iters) / ms / 1e9,
+                                           1)
+    out["mfma_vector_loop"] = ("the MFMA loop plus 16 exp2 and 48 FMAs per 16 MFMAs on "
+                               "independent registers (a fine-kernel wave-step's vector work), "
+                               "2 waves per workgroup, 4 workgroups and 2 waves per SIMD as in "
+                               "the fine kernel, 2048 workgroups")
     n = 16384
     a = torch.randn((n, n), generator=gen, device=dev).to(torch.bfloat16)
     b = torch.randn((n, n), generator=gen, device=dev).to(torch.bfloat16)
@@ -723,7 +751,8 @@ def main():
                                      / PEAK_BF16_TFLOPS, 2),
         "clock_during_fwd": clock_fwd,
         "bf16_ceilings": dict(ceilings, fwd_pct_of_mfma_loop=round(
-            100 * tflops / ceilings["mfma_loop_tflops"], 1), fwd_pct_of_gemm_bf16=round(
+            100 * tflops / ceilings["mfma_loop_tflops"], 1), fwd_pct_of_mfma_vector_loop=round(
+            100 * tflops / ceilings["mfma_vector_loop_tflops"], 1), fwd_pct_of_gemm_bf16=round(
             100 * tflops / ceilings["gemm_bf16_16384_tflops"], 1)),
         "fwd_finite": finite,
         "dense": {"topk": Nc, "ms": round(dense_ms, 4), "tflop": round(dense_flops / 1e12, 3),

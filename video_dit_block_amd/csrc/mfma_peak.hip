@@ -9,8 +9,11 @@
 // shader cycle counter (s_memtime), launched on a second stream beside a timed
 // loop; the ratio of the two counts is the clock the loop ran at. (3) An LDS
 // read pattern with and without bank conflicts, a control for the profiler's
-// bank-conflict counter. Built into
-// its own library (libvsa_probe.so), loaded only by the benchmark.
+// bank-conflict counter. (4) The MFMA loop with the fine kernel's vector
+// work beside its MFMAs, at the fine kernel's occupancy: the rate the matrix
+// units reach with that instruction mix when nothing else (loads, barriers,
+// dependent accumulators) holds them. Built into its own library
+// (libvsa_probe.so), loaded only by the benchmark.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -99,6 +102,55 @@ __global__ __launch_bounds__(64) void lds_conflict_kernel(int stride, int iters,
   out[(size_t)blockIdx.x * 64 + lane] = acc;
 }
 
+// (4): 2-wave workgroups holding 40 KiB of LDS each, so 4 workgroups and 2
+// waves per SIMD share a CU as in the fine kernel. Per 16 MFMAs (the same
+// operands and accumulators as mfma_peak_kernel) every lane also runs 16
+// exp2 and 48 FMAs on 16 registers that no MFMA reads, about the vector work
+// of one fine-kernel wave-step (16 exponentials and some 50 other vector
+// instructions). `src` as for mfma_peak_kernel; out: blocks * 128 floats.
+constexpr int kMixThreads = 128;
+constexpr int kMixLdsBytes = 40960;
+constexpr int kMixExp = 16, kMixFma = 48;
+
+__global__ __launch_bounds__(kMixThreads) void mfma_mix_kernel(const uint4* __restrict__ src,
+                                                               int n_src_slots, int iters,
+                                                               float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kMixLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint4* s = src + (size_t)(blockIdx.x % n_src_slots) * (kLdsBytes / 16);
+  for (int i = tid; i < kLdsBytes / 16; i += kMixThreads) reinterpret_cast<uint4*>(lds)[i] = s[i];
+  if (tid == 0) lds[kMixLdsBytes - 1] = 1;  // the whole allocation is in use
+  __syncthreads();
+  // each wave reads 16-byte operands from 8 KiB in its own half of the random
+  // 32 KiB
+  const uint8_t* base = lds + wave * 16384 + lane * 16;
+  floatx16 acc[4] = {};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 0.001f * (float)(lane + i);
+  const float c = 0.9999f, d = -0.0001f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < kMfmaPerIter; ++m) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(base + ((m + it) & 3) * 1024);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(base + 4096 + ((m + 2 * it) & 3) * 1024);
+      acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
+      if (m < kMixExp) x[m] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[m], c, d));
+#pragma unroll
+      for (int f = 0; f < kMixFma / kMfmaPerIter; ++f)
+        x[(m + 5 * f + 1) & 15] = __builtin_fmaf(x[(m + 5 * f + 1) & 15], c, d);
+    }
+  }
+  float r = (float)lds[kMixLdsBytes - 1];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r += acc[j][i];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r += x[i];
+  out[(size_t)blockIdx.x * kMixThreads + tid] = r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +200,24 @@ int32_t vsa_probe_mfma(const void* src, int32_t n_src_slots, int32_t blocks, int
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
                      n_src_slots, iters, out);
   return (int32_t)hipGetLastError();
+}
+
+// Launches the loop with vector work (4) on `stream`: `blocks` workgroups of
+// 2 waves; src as for vsa_probe_mfma; out: device float buffer of blocks * 128
+// entries. Returns 0, or the hipError_t of the launch.
+int32_t vsa_probe_mfma_mix(const void* src, int32_t n_src_slots, int32_t blocks, int32_t iters,
+                           float* out, void* stream) {
+  if (src == nullptr || out == nullptr || n_src_slots <= 0 || blocks <= 0 || iters <= 0)
+    return (int32_t)hipErrorInvalidValue;
+  hipLaunchKernelGGL(mfma_mix_kernel, dim3(blocks), dim3(kMixThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
+                     n_src_slots, iters, out);
+  return (int32_t)hipGetLastError();
+}
+
+// MFMA FLOP of one launch of (4): blocks * 2 waves * iters * 16 MFMAs * 32768.
+double vsa_probe_mfma_mix_flop(int32_t blocks, int32_t iters) {
+  return (double)blocks * 2.0 * iters * kMfmaPerIter * 32.0 * 32.0 * 16.0 * 2.0;
 }
 
 }  // extern "C"
