@@ -395,10 +395,46 @@ __global__ __launch_bounds__(kCvtThreads) void vfix_kernel(
 // splits each split's sweep rotates the same way inside the split's range,
 // by the item's own dispatch position.
 constexpr int kListSortCap = 1024;
+constexpr int kListRegSort = 256;  // rows up to this long sort in registers
 constexpr int kListPad = 4;
 constexpr int kQuarter = 16;  // rows per quarter
 // fine-kernel units resident per XCD on MI355X: 32 CUs x 4 workgroups
 constexpr int kSweepWindow = 128;
+
+// Bitonic sort of 64 R keys held by one wave, key p = lane + 64 r in
+// register r: a compare-exchange with a partner less than 64 positions away
+// is a cross-lane swap (__shfl_xor), one 64 or more away is inside the lane.
+// Ascending; no LDS and no barriers.
+template <int R>
+__device__ __forceinline__ void wave_bitonic_sort(int (&v)[R], int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64 * R; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 64) {
+        const int rs = stride / 64;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r & rs) continue;  // r is the lower position of its pair
+          const int p = lane + 64 * r;
+          const int a = v[r], c = v[r | rs];
+          const bool asc = (p & size) == 0;
+          v[r] = asc ? min(a, c) : max(a, c);
+          v[r | rs] = asc ? max(a, c) : min(a, c);
+        }
+      } else {
+        const bool lower = (lane & stride) == 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int p = lane + 64 * r;
+          const int w = __shfl_xor(v[r], stride, 64);
+          const bool take_min = lower == ((p & size) == 0);
+          v[r] = take_min ? min(v[r], w) : max(v[r], w);
+        }
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(64) void tiles_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ valid,
@@ -421,7 +457,25 @@ __global__ __launch_bounds__(64) void tiles_kernel(
   auto id_at = [&](int i) __attribute__((always_inline)) -> int {
     return min(max(sel[i], 0), Nkv - 1);
   };
-  if (sorted) {
+  // rows of up to kListRegSort ids sort in registers (64, 128 or 256 keys,
+  // padded with INT_MAX), longer ones through LDS
+  auto reg_sort = [&](auto Rc) __attribute__((always_inline)) {
+    constexpr int R = decltype(Rc)::value;
+    int v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = lane + 64 * r < topk ? id_at(lane + 64 * r) : 0x7FFFFFFF;
+    wave_bitonic_sort<R>(v, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) keys[lane + 64 * r] = v[r];
+    __syncthreads();
+  };
+  if (sorted && topk <= 64) {
+    reg_sort(std::integral_constant<int, 1>{});
+  } else if (sorted && topk <= 128) {
+    reg_sort(std::integral_constant<int, 2>{});
+  } else if (sorted && topk <= kListRegSort) {
+    reg_sort(std::integral_constant<int, 4>{});
+  } else if (sorted) {
     int n2 = 1;
     while (n2 < topk) n2 <<= 1;
     for (int i = lane; i < n2; i += 64) keys[i] = i < topk ? id_at(i) : 0x7FFFFFFF;
