@@ -311,6 +311,7 @@ __global__ __launch_bounds__(256) void vscale_kernel(const uint32_t* __restrict_
   const int h = blockIdx.x, b = blockIdx.y;
   const uint32_t* __restrict__ vm = vmax + (size_t)b * n_wg * NH + h;
   uint32_t m = 0;
+#pragma unroll 8  // several loads in flight per thread
   for (int i = threadIdx.x; i < n_wg; i += 256) m = max(m, vm[(size_t)i * NH]);
   for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
   if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = m;
