@@ -112,3 +112,28 @@ def test_tile_lists_of_dense_rows_are_not_rotated():
             torch.from_numpy(vbs).cuda(), workspace=ws)
     torch.cuda.synchronize()
     assert _check_lists(ws, B, Nq, Nkv, NH, D, Nkv, idx, None, vbs, 1) == 0
+
+
+@pytest.mark.parametrize("topk", [64, 65, 128, 129, 256, 257])
+@pytest.mark.parametrize("splits", [1, 2])
+def test_tile_lists_across_the_sort_paths(topk, splits):
+    """Rows of up to 64, 128 and 256 ids are sorted in registers (1, 2 or 4
+    keys per lane), longer ones through LDS: every path gives the same
+    lists (each selected quarter once, one wrapped ascending sweep)."""
+    rng = np.random.default_rng(80 + topk + splits)
+    B, Nq, Nkv, NH, D = 1, 8, 300, 2, 64
+    f32 = lambda *s: rng.standard_normal(s, dtype=np.float32)
+    q = synth.bf16_bits_from_f32(f32(B, Nq * 64, NH, D))
+    k = synth.bf16_bits_from_f32(f32(B, Nkv * 64, NH, D))
+    v = synth.bf16_bits_from_f32(f32(B, Nkv * 64, NH, D))
+    vbs = rng.choice([1, 8, 16, 17, 33, 48, 64], size=Nkv).astype(np.int32)
+    idx = np.stack([np.stack([rng.permutation(Nkv)[:topk] for _ in range(Nq)])
+                    for _ in range(NH)])[None].astype(np.int32)
+    assert vsa.fwd_splits(Nkv, D, topk, splits) == splits
+    ws = torch.zeros(vsa.fwd_workspace_bytes(B, Nq, Nkv, NH, D, topk, splits), dtype=torch.uint8,
+                     device="cuda")
+    vsa.fwd_lut(to_gpu_bf16(q), to_gpu_bf16(k), to_gpu_bf16(v), torch.from_numpy(idx).cuda(),
+                None, torch.from_numpy(vbs).cuda(), workspace=ws, kv_splits=splits)
+    torch.cuda.synchronize()
+    rotated = _check_lists(ws, B, Nq, Nkv, NH, D, topk, idx, None, vbs, splits)
+    print(f"[tile lists topk={topk} splits={splits}] rotated sweeps: {rotated}", flush=True)
